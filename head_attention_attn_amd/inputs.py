@@ -1,0 +1,83 @@
+"""Seeded synthetic inputs for the attention path.
+
+This module holds no attention arithmetic: it only names the workloads and
+draws their inputs, so that the HIP library and the fp64 oracle are fed the
+very same values.  Recipe: one CPU ``torch.Generator`` seeded with ``seed``;
+Q, K, V, dO drawn in that order with ``torch.randn(shape, float32)``; for bf16
+workloads each tensor is then rounded to bfloat16 (round to nearest even).
+The oracle widens exactly these values to float64.
+
+Workloads (shapes after the pages' own models; the activations themselves
+are synthetic i.i.d. N(0, 1)):
+
+* tiny_exact_fp32 -- a small exact-check case the oracle finishes instantly.
+* block_local_hiera -- Hiera-style mask-unit attention at the first stage of
+  a 224x224 input: a 56x56 = 3136-token grid split into 49 independent
+  windows of 64 contiguous tokens, batch 128 ("hiera-optim 0.1.0", Results:
+  Hiera-Base 224x224, B=128; sdist mask_unit.py: windows as independent
+  batches).
+* global_vision -- Hiera's global-attention stage on a 14x14 grid.
+* causal_lm -- causal attention of a 20-head, d=128 LLaMA at N=8192
+  ("IHA-CUDA", End-to-End Training Benchmark).
+* sliding_pseudo_head -- causal sliding window W = 1024 (WSL = 1023) over
+  20 heads x 4 pseudo-heads at N=4096 ("IHA-CUDA", FLOP Matching).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, asdict
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str          # "bf16" or "fp32"
+    mask: str           # "none" | "causal" | "sliding" | "block"
+    window: int = 0
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) as the fp32 value handed to both sides."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32))
+
+    def as_dict(self) -> dict:
+        return asdict(self)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tiny_exact_fp32", 1, 2, 128, 128, 64, "fp32", "none"),
+        Workload("block_local_hiera", 128, 1, 3136, 3136, 96, "bf16", "block", 64),
+        Workload("global_vision", 128, 4, 196, 196, 96, "bf16", "none"),
+        Workload("causal_lm", 1, 20, 8192, 8192, 128, "bf16", "causal"),
+        Workload("sliding_pseudo_head", 1, 80, 4096, 4096, 128, "bf16", "sliding", 1024),
+    )
+}
+
+TORCH_DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def make_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str = "bf16",
+                seed: int = 0):
+    """Return CPU tensors (q, k, v, do) drawn as the module docstring states."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((B, H, Nq, d), dtype=torch.float32, generator=g)
+    k = torch.randn((B, H, Nk, d), dtype=torch.float32, generator=g)
+    v = torch.randn((B, H, Nk, d), dtype=torch.float32, generator=g)
+    do = torch.randn((B, H, Nq, d), dtype=torch.float32, generator=g)
+    tdt = TORCH_DTYPES[dtype]
+    if tdt is not torch.float32:
+        q, k, v, do = (t.to(tdt) for t in (q, k, v, do))
+    return q, k, v, do
+
+
+def workload_inputs(w: Workload, seed: int = 0):
+    return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, seed)

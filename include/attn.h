@@ -1,0 +1,161 @@
+/*
+ * attn.h -- C ABI of libattn: fused multi-head scaled-dot-product attention,
+ * forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ *   O = softmax(scale * Q K^T + mask) V        (per batch b, head h)
+ *
+ * computed with an online softmax (running row max and row sum, rescaled per
+ * key tile), plus the gradient of any scalar loss L with respect to Q, K, V
+ * given dO = dL/dO.
+ *
+ * Where the operations come from (cited by page title and section):
+ *   - Mask-unit (block-local) attention: "hiera-optim 0.1.0" sdist,
+ *     hiera_optim/attention/mask_unit.py, MaskUnitAttentionFast.forward --
+ *     tokens split into independent windows, a dense softmax attention inside
+ *     each window, default scale head_dim^-0.5.
+ *   - Causal sliding window: "IHA-CUDA: Interleaved Head Attention Kernels for
+ *     Hopper GPUs", section "FLOP Matching" -- a window of W = WSL + 1 keys
+ *     including the diagonal.
+ *   - Backward split into a row-statistics pre-pass (dPsum, lse), a dK/dV pass
+ *     and a dQ pass, with visited tile ranges computed per causal/windowed
+ *     mask and fully masked tiles never visited: same page, section
+ *     "Repository Structure" (flash_bwd_preprocess, block_info, mask,
+ *     softmax).  Here dQ is produced by its own pass over key tiles instead of
+ *     an atomic fp32 accumulator, so results are bitwise deterministic.
+ *   - Caller-owned outputs, base-pointer alignment checks and device gating
+ *     follow the review points of "flashdreams.accelerated API v0 - #486"
+ *     (output storage aliasing a cached buffer; base pointer alignment;
+ *     rejecting unsupported devices up front instead of failing mid-run).
+ *
+ * Layouts (all tensors contiguous, row-major, element type `dtype` except lse
+ * and the workspace, which are fp32):
+ *     Q, O, dO, dQ : [B][H][Nq][d]
+ *     K, V, dK, dV : [B][H][Nk][d]
+ *     lse          : [B][H][Nq]      natural-log logsumexp of the scaled,
+ *                                    masked scores of each query row
+ * Accumulation is always fp32.  bf16 outputs are rounded to nearest even.
+ *
+ * Visibility of key j to query i (absolute indices, top-left aligned):
+ *     ATTN_MASK_NONE     every key
+ *     ATTN_MASK_CAUSAL   j <= i
+ *     ATTN_MASK_SLIDING  i - window < j <= i        (window >= 1)
+ *     ATTN_MASK_BLOCK    i / window == j / window   (integer division; needs
+ *                                                    Nq == Nk, Nk % window == 0)
+ * A query row that sees no key gets O = 0, lse = -inf, dQ = 0.
+ *
+ * Ownership: the caller allocates every buffer, including the backward
+ * workspace.  The library allocates no device memory, keeps no per-call
+ * state, and is reentrant across streams and host threads.  Outputs are fully
+ * overwritten (never accumulated into) and must not overlap any input or each
+ * other.  Every base pointer must be 16-byte aligned.
+ *
+ * Errors: every entry point validates all arguments before touching the
+ * device.  A nonzero status means nothing was enqueued and no output was
+ * written -- except ATTN_ERR_LAUNCH, the HIP launch status after an enqueue.
+ * ATTN_OK means the work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) with no host synchronisation; device faults surface at the
+ * caller's next synchronisation.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1 };
+
+enum attn_mask {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_SLIDING = 2,
+  ATTN_MASK_BLOCK = 3
+};
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, size < 1, bad mask/window      */
+  ATTN_ERR_UNSUPPORTED = 2, /* dtype or head dim d not built (d in 64/96/128) */
+  ATTN_ERR_MISALIGNED = 3,  /* a base pointer is not 16-byte aligned          */
+  ATTN_ERR_WORKSPACE = 4,   /* workspace null or smaller than required        */
+  ATTN_ERR_ALIAS = 5,       /* an output overlaps an input or another output  */
+  ATTN_ERR_DEVICE = 6,      /* current device is not gfx950, or HIP query failed */
+  ATTN_ERR_LAUNCH = 7       /* a kernel launch reported an error              */
+};
+
+/*
+ * attn_fwd -- forward pass.
+ *   dtype        ATTN_BF16 or ATTN_FP32 (element type of q, k, v, o)
+ *   B, H         batch and head count (>= 1)
+ *   Nq, Nk       query and key sequence lengths (>= 1)
+ *   d            head dimension: 64, 96 or 128
+ *   scale        multiplier of Q K^T (e.g. 1/sqrt(d))
+ *   mask, window mask mode and its window (ignored for NONE and CAUSAL)
+ *   q, k, v      device inputs, layouts above
+ *   o            device output [B][H][Nq][d], dtype
+ *   lse          device output [B][H][Nq], fp32
+ *   stream       hipStream_t to enqueue on (NULL = default stream)
+ * Returns an attn_status.
+ */
+int attn_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+             float scale, int mask, int64_t window,
+             const void* q, const void* k, const void* v,
+             void* o, float* lse, void* stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs: one
+ * fp32 per query row (the row sums D_i = sum_c dO[i][c] * O[i][c], the
+ * "dPsum" of the backward pre-pass), rounded up to 256 bytes.  Returns 0 if
+ * B, H or Nq is < 1.
+ */
+size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
+
+/*
+ * attn_bwd -- backward pass: dQ, dK, dV of L given dO = dL/dO.
+ *   q, k, v, o, lse  the forward inputs and outputs (o and lse as written by
+ *                    attn_fwd for the same arguments)
+ *   dout             dO, [B][H][Nq][d], dtype
+ *   dq, dk, dv       device outputs, layouts of q, k, v
+ *   workspace        device scratch of >= attn_bwd_workspace_size(B, H, Nq)
+ *                    bytes, caller-owned; contents on entry are ignored
+ * Other arguments as attn_fwd.  Three kernels run in stream order: the row-sum
+ * pre-pass, the dK/dV pass (one workgroup per key tile, looping over visible
+ * query tiles) and the dQ pass (one workgroup per query tile, looping over
+ * visible key tiles).
+ */
+int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+             float scale, int mask, int64_t window,
+             const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout,
+             void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_check_fwd / attn_check_bwd -- the argument validation of attn_fwd /
+ * attn_bwd alone: no device query, no launch.  Same arguments (the stream is
+ * not needed).  Returns the status the entry point would return before
+ * enqueueing, except that the device check (ATTN_ERR_DEVICE) is not made.
+ */
+int attn_check_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                   float scale, int mask, int64_t window,
+                   const void* q, const void* k, const void* v,
+                   const void* o, const float* lse);
+
+int attn_check_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                   float scale, int mask, int64_t window,
+                   const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout,
+                   const void* dq, const void* dk, const void* dv,
+                   const void* workspace, size_t workspace_bytes);
+
+/* attn_status_string -- static, human-readable name of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */
