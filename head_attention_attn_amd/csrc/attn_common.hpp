@@ -1,0 +1,127 @@
+// attn_common.hpp -- shared definitions of the gfx950 attention kernels:
+// launch parameters, the per-row / per-key visibility intervals that drive
+// tile ranges and masking, and thin wrappers over the CDNA4 MFMA and LDS
+// transpose-read builtins.
+//
+// Visibility (all four mask modes) is an interval per query row i:
+//     key j is visible to i  <=>  row_lo(i) <= j < row_hi(i)
+//   none    [0, Nk)
+//   causal  [0, min(i + 1, Nk))
+//   sliding [max(0, i - W + 1), min(i + 1, Nk))     W keys incl. the diagonal
+//                                                   ("IHA-CUDA", FLOP Matching)
+//   block   [floor(i/W)*W, min(floor(i/W)*W + W, Nk))   independent windows
+//                                                   ("hiera-optim" sdist,
+//                                                   MaskUnitAttentionFast)
+// and, equivalently, an interval of queries per key j:
+//     col_lo(j) <= i < col_hi(j).
+// Both bounds are non-decreasing in i (resp. j), so the keys a block of rows
+// [a, b) can see are [row_lo(a), row_hi(b-1)), and a rows x keys tile is fully
+// visible iff its keys lie in [row_lo(b-1), row_hi(a)).  This is the tile-range
+// computation ("IHA-CUDA", Repository Structure: block_info / mask) written as
+// intervals.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define ATTN_HD __host__ __device__ __forceinline__
+#else
+#define ATTN_HD inline
+#endif
+
+namespace attn {
+
+enum MaskMode : int { kNone = 0, kCausal = 1, kSliding = 2, kBlock = 3 };
+
+struct MaskGeom {
+  int mode;
+  int nq, nk;
+  int window;  // W for sliding / block; unused otherwise
+
+  ATTN_HD int imin(int a, int b) const { return a < b ? a : b; }
+  ATTN_HD int imax(int a, int b) const { return a > b ? a : b; }
+
+  // keys visible to query row i: [row_lo(i), row_hi(i))
+  ATTN_HD int row_lo(int i) const {
+    if (mode == kSliding) return imax(0, i - window + 1);
+    if (mode == kBlock) return (i / window) * window;
+    return 0;
+  }
+  ATTN_HD int row_hi(int i) const {
+    if (mode == kCausal || mode == kSliding) return imin(i + 1, nk);
+    if (mode == kBlock) return imin((i / window) * window + window, nk);
+    return nk;
+  }
+  // queries that see key j: [col_lo(j), col_hi(j))
+  ATTN_HD int col_lo(int j) const {
+    if (j >= nk) return nq;
+    if (mode == kCausal || mode == kSliding) return imin(j, nq);
+    if (mode == kBlock) return imin((j / window) * window, nq);
+    return 0;
+  }
+  ATTN_HD int col_hi(int j) const {
+    if (j >= nk) return nq;
+    if (mode == kSliding) return imin(j + window, nq);
+    if (mode == kBlock) return imin((j / window) * window + window, nq);
+    return nq;
+  }
+  // keys visible to any row of [a, b) (b > a): [lo, hi), possibly empty
+  ATTN_HD void key_range(int a, int b, int* lo, int* hi) const {
+    *lo = row_lo(a);
+    *hi = row_hi(b - 1);
+  }
+  // queries that see any key of [a, b) (b > a)
+  ATTN_HD void query_range(int a, int b, int* lo, int* hi) const {
+    *lo = col_lo(a);
+    *hi = col_hi(imin(b, nk) - 1);
+    if (a >= nk) *hi = *lo;
+  }
+  // every (row, key) of rows [a, b) x keys [j0, j1) visible; needs b <= nq, j1 <= nk
+  ATTN_HD bool tile_full(int a, int b, int j0, int j1) const {
+    if (b > nq || j1 > nk) return false;
+    return j0 >= row_lo(b - 1) && j1 <= row_hi(a);
+  }
+};
+
+// ---------------------------------------------------------------- launches
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, nq, nk;
+  float scale;
+  MaskGeom mg;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;  // workspace: D_i = sum_c dO[i][c] * O[i][c], fp32 [B][H][Nq]
+  int B, H, nq, nk;
+  float scale;
+  MaskGeom mg;
+};
+
+}  // namespace attn
+
+#if defined(__HIPCC__)
+namespace attn {
+// Launchers, one per dtype; each picks its kernel instantiation from (d, mask).
+// They return the hipError_t of the launch(es) as an int.
+int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
+int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s);
+int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s);
+int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s);
+}  // namespace attn
+#endif

@@ -1,0 +1,207 @@
+// attn_fp32.hip -- fp32 attention kernels (forward, row-sum pre-pass, dK/dV,
+// dQ) on the vector ALUs.
+//
+// fp32 inputs carry a 1e-5 accuracy budget, which bf16 MFMA operands cannot
+// meet, and the fp32 workloads are small exact-check cases; so this path uses
+// plain fp32 FMAs: a group of 16 lanes owns one row (a query row in the
+// forward and dQ kernels, a key row in the dK/dV kernel), each lane holding
+// D/16 of its d entries; dot products reduce across the group with
+// cross-lane xor shuffles.  The visible range of every row is the interval of
+// attn_common.hpp, so fully masked keys are never visited.  The forward uses
+// the online softmax (running max and sum, rescaling the accumulator) in
+// natural-log units; the backward recomputes P = exp(s - lse).
+#include "attn_common.hpp"
+
+namespace attn {
+
+namespace {
+
+constexpr int kGroup = 16;       // lanes per row
+constexpr int kRowsPerBlock = 16;
+
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 8, kGroup);
+  x += __shfl_xor(x, 4, kGroup);
+  x += __shfl_xor(x, 2, kGroup);
+  x += __shfl_xor(x, 1, kGroup);
+  return x;
+}
+
+template <int D>
+__device__ __forceinline__ void load_slice(float (&dst)[D / kGroup], const float* row, int li) {
+#pragma unroll
+  for (int e = 0; e < D / kGroup; ++e) dst[e] = row[li + kGroup * e];
+}
+
+template <int D>
+__device__ __forceinline__ float dot_slice(const float (&x)[D / kGroup], const float* row, int li) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < D / kGroup; ++e) s = fmaf(x[e], row[li + kGroup * e], s);
+  return group_sum(s);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdArgs a) {
+  constexpr int E = D / kGroup;
+  const int li = threadIdx.x & (kGroup - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
+  const int64_t rows = (int64_t)a.B * a.H * a.nq;
+  if (row >= rows) return;  // whole 16-lane groups leave together
+  const int64_t bh = row / a.nq;
+  const int i = (int)(row % a.nq);
+  const float* K = (const float*)a.k + bh * a.nk * D;
+  const float* V = (const float*)a.v + bh * a.nk * D;
+  float q[E], acc[E];
+  load_slice<D>(q, (const float*)a.q + row * D, li);
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int lo = a.mg.row_lo(i), hi = a.mg.row_hi(i);
+  for (int j = lo; j < hi; ++j) {
+    const float s = a.scale * dot_slice<D>(q, K + (int64_t)j * D, li);
+    const float mnew = fmaxf(m, s);
+    const float alpha = expf(m - mnew);   // m = -inf on the first key -> 0
+    const float p = expf(s - mnew);
+    l = l * alpha + p;
+    const float* vr = V + (int64_t)j * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(p, vr[li + kGroup * e], acc[e] * alpha);
+    m = mnew;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float* O = (float*)a.o + row * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) O[li + kGroup * e] = acc[e] * inv;
+  if (li == 0) a.lse[row] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dsum_fp32_kernel(const float* __restrict__ o,
+                                                        const float* __restrict__ dout,
+                                                        float* __restrict__ dsum, int64_t rows) {
+  constexpr int E = D / kGroup;
+  const int li = threadIdx.x & (kGroup - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
+  if (row >= rows) return;
+  float x[E];
+  load_slice<D>(x, o + row * D, li);
+  const float s = dot_slice<D>(x, dout + row * D, li);
+  if (li == 0) dsum[row] = s;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dq_fp32_kernel(BwdArgs a) {
+  constexpr int E = D / kGroup;
+  const int li = threadIdx.x & (kGroup - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
+  const int64_t rows = (int64_t)a.B * a.H * a.nq;
+  if (row >= rows) return;
+  const int64_t bh = row / a.nq;
+  const int i = (int)(row % a.nq);
+  const float* K = (const float*)a.k + bh * a.nk * D;
+  const float* V = (const float*)a.v + bh * a.nk * D;
+  float q[E], g[E], acc[E];
+  load_slice<D>(q, (const float*)a.q + row * D, li);
+  load_slice<D>(g, (const float*)a.dout + row * D, li);
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const float lse = a.lse[row], dsv = a.dsum[row];
+  const int lo = a.mg.row_lo(i), hi = a.mg.row_hi(i);
+  for (int j = lo; j < hi; ++j) {
+    const float* kr = K + (int64_t)j * D;
+    const float p = expf(a.scale * dot_slice<D>(q, kr, li) - lse);
+    const float ds = p * (dot_slice<D>(g, V + (int64_t)j * D, li) - dsv);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, kr[li + kGroup * e], acc[e]);
+  }
+  float* dQ = (float*)a.dq + row * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dQ[li + kGroup * e] = acc[e] * a.scale;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_fp32_kernel(BwdArgs a) {
+  constexpr int E = D / kGroup;
+  const int li = threadIdx.x & (kGroup - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
+  const int64_t rows = (int64_t)a.B * a.H * a.nk;
+  if (row >= rows) return;
+  const int64_t bh = row / a.nk;
+  const int j = (int)(row % a.nk);
+  const float* Q = (const float*)a.q + bh * a.nq * D;
+  const float* dO = (const float*)a.dout + bh * a.nq * D;
+  const float* LSE = a.lse + bh * a.nq;
+  const float* DS = a.dsum + bh * a.nq;
+  float k[E], v[E], dk[E], dv[E];
+  load_slice<D>(k, (const float*)a.k + row * D, li);
+  load_slice<D>(v, (const float*)a.v + row * D, li);
+#pragma unroll
+  for (int e = 0; e < E; ++e) dk[e] = dv[e] = 0.f;
+  const int lo = a.mg.col_lo(j), hi = a.mg.col_hi(j);
+  for (int i = lo; i < hi; ++i) {
+    const float* qr = Q + (int64_t)i * D;
+    const float* gr = dO + (int64_t)i * D;
+    const float p = expf(a.scale * dot_slice<D>(k, qr, li) - LSE[i]);
+    const float ds = p * (dot_slice<D>(v, gr, li) - DS[i]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      dv[e] = fmaf(p, gr[li + kGroup * e], dv[e]);
+      dk[e] = fmaf(ds, qr[li + kGroup * e], dk[e]);
+    }
+  }
+  float* dK = (float*)a.dk + row * D;
+  float* dV = (float*)a.dv + row * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    dK[li + kGroup * e] = dk[e] * a.scale;
+    dV[li + kGroup * e] = dv[e];
+  }
+}
+
+inline unsigned blocks_for(int64_t rows) {
+  return (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+}
+
+template <int D>
+int fwd_d(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_fp32_kernel<D>), dim3(blocks_for((int64_t)a.B * a.H * a.nq)), dim3(256),
+                     0, s, a);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int bwd_d(const BwdArgs& a, hipStream_t s) {
+  const int64_t qrows = (int64_t)a.B * a.H * a.nq, krows = (int64_t)a.B * a.H * a.nk;
+  hipLaunchKernelGGL((dsum_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s,
+                     (const float*)a.o, (const float*)a.dout, a.dsum, qrows);
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  hipLaunchKernelGGL((dkdv_fp32_kernel<D>), dim3(blocks_for(krows)), dim3(256), 0, s, a);
+  err = (int)hipGetLastError();
+  if (err) return err;
+  hipLaunchKernelGGL((dq_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return fwd_d<64>(a, s);
+    case 96: return fwd_d<96>(a, s);
+    case 128: return fwd_d<128>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return bwd_d<64>(a, s);
+    case 96: return bwd_d<96>(a, s);
+    case 128: return bwd_d<128>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -1,0 +1,86 @@
+// mfma.hpp -- CDNA4 (gfx950) building blocks for the bf16 attention kernels.
+//
+// v_mfma_f32_32x32x16_bf16 lane layout (checked on gfx950 hardware):
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) + s, s = 0..7
+//   B (16 x 32): lane l holds col l%32, k = 8*(l/32) + s
+//   C (32 x 32): lane l holds col l%32, rows 8*i + 4*(l/32) + j in acc[4*i + j]
+// The contraction index k may be permuted freely as long as A and B agree;
+// the kernels use that to feed an accumulator straight back in as an operand.
+//
+// ds_read_b64_tr_b16 (LDS transpose read, 16-bit elements): within each group
+// of 16 lanes, with source lane 4*e + r pointing at 4 consecutive elements
+// M[4e + r][0..3], destination lane i receives M[4e + i/4][i%4] for e = 0..3.
+// Pointing source lane 4e + r at row (r0 + e), column (c0 + 4r) of a row-major
+// tile therefore gives lane i the four elements (r0 + e, c0 + i), e = 0..3: a
+// column read of a row-major tile, which is what an MFMA operand whose
+// contraction runs along the tile's rows needs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte LDS read of 8 consecutive bf16 (ds_read_b128)
+__device__ __forceinline__ bf16x8 lds_read8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposed operand read.  `tile` is a row-major bf16 tile in LDS with row
+// stride `stride` elements.  Returns, for this lane, the 8 contraction
+// elements of an MFMA A/B operand whose free index is the tile column
+// c0 + (lane % 32) and whose contraction runs over tile rows: slots 0..3 are
+// rows r0 + 4*g + e, slots 4..7 are rows r0 + 8 + 4*g + e (g = lane / 32,
+// e = 0..3).  This row order is exactly the row order in which a 32x32
+// accumulator stores a 16-row chunk (rows 8*i + 4*g + j, i = 2c, 2c + 1), so
+// it pairs with acc_chunk() below.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* tile, int stride, int r0, int c0,
+                                               int lane) {
+  const int grp = lane >> 4;        // 16-lane group 0..3
+  const int li = lane & 15;
+  const int e = li >> 2, r = li & 3;
+  const int g = grp >> 1;           // contraction-slot group
+  const int half = grp & 1;         // which 16 of the 32 columns
+  const uint16_t* p0 = tile + (r0 + 4 * g + e) * stride + c0 + 16 * half + 4 * r;
+  const uint16_t* p1 = p0 + 8 * stride;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Accumulator entries 8c .. 8c+7 of a 32x32 tile, rounded to bf16: the rows
+// (8*(2c) + 4g + j, 8*(2c+1) + 4g + j) of chunk c in the order lds_read_tr8
+// uses, ready to be the other operand of a contraction over those rows.
+__device__ __forceinline__ bf16x8 acc_chunk(const f32x16& acc, int c) {
+  f32x8 v;
+  #pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = acc[8 * c + s];
+  return __builtin_convertvector(v, bf16x8);
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  bf16x4 h = __builtin_convertvector(v, bf16x4);
+  return __builtin_bit_cast(uint2, h);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+}  // namespace attn

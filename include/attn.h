@@ -62,6 +62,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__GNUC__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -100,7 +106,7 @@ enum attn_status {
  *   stream       hipStream_t to enqueue on (NULL = default stream)
  * Returns an attn_status.
  */
-int attn_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+ATTN_API int attn_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
              float scale, int mask, int64_t window,
              const void* q, const void* k, const void* v,
              void* o, float* lse, void* stream);
@@ -111,7 +117,7 @@ int attn_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
  * "dPsum" of the backward pre-pass), rounded up to 256 bytes.  Returns 0 if
  * B, H or Nq is < 1.
  */
-size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
+ATTN_API size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
 
 /*
  * attn_bwd -- backward pass: dQ, dK, dV of L given dO = dL/dO.
@@ -126,7 +132,7 @@ size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
  * query tiles) and the dQ pass (one workgroup per query tile, looping over
  * visible key tiles).
  */
-int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+ATTN_API int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
              float scale, int mask, int64_t window,
              const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout,
@@ -139,12 +145,12 @@ int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
  * not needed).  Returns the status the entry point would return before
  * enqueueing, except that the device check (ATTN_ERR_DEVICE) is not made.
  */
-int attn_check_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+ATTN_API int attn_check_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                    float scale, int mask, int64_t window,
                    const void* q, const void* k, const void* v,
                    const void* o, const float* lse);
 
-int attn_check_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+ATTN_API int attn_check_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                    float scale, int mask, int64_t window,
                    const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dout,
@@ -152,7 +158,7 @@ int attn_check_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int6
                    const void* workspace, size_t workspace_bytes);
 
 /* attn_status_string -- static, human-readable name of a status code. */
-const char* attn_status_string(int status);
+ATTN_API const char* attn_status_string(int status);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,104 @@
+// Brute-force check of the visibility intervals and tile predicates of
+// attn_common.hpp (host build, no GPU).  Exit status 0 iff every check holds.
+#include <cstdio>
+#include <cstdlib>
+
+#include "attn_common.hpp"
+
+using attn::MaskGeom;
+
+static bool sees(int mode, int W, int nk, int i, int j) {
+  if (j < 0 || j >= nk) return false;
+  switch (mode) {
+    case attn::kNone: return true;
+    case attn::kCausal: return j <= i;
+    case attn::kSliding: return i - W < j && j <= i;
+    case attn::kBlock: return i / W == j / W;
+  }
+  return false;
+}
+
+static int fails = 0;
+#define CHECK(c, ...)                                   \
+  do {                                                  \
+    if (!(c)) {                                         \
+      if (fails < 20) std::printf(__VA_ARGS__);         \
+      ++fails;                                          \
+    }                                                   \
+  } while (0)
+
+static void check(int mode, int W, int nq, int nk) {
+  MaskGeom g{mode, nq, nk, W};
+  for (int i = 0; i < nq; ++i)
+    for (int j = 0; j < nk; ++j) {
+      const bool v = sees(mode, W, nk, i, j);
+      CHECK(v == (g.row_lo(i) <= j && j < g.row_hi(i)), "row interval m%d W%d %dx%d i%d j%d\n", mode, W,
+            nq, nk, i, j);
+      CHECK(v == (g.col_lo(j) <= i && i < g.col_hi(j)), "col interval m%d W%d %dx%d i%d j%d\n", mode, W,
+            nq, nk, i, j);
+    }
+  const int steps[] = {1, 3, 4, 7, 16, 32};
+  for (int bs : steps) {
+    for (int a = 0; a < nq; a += bs) {
+      const int b = a + bs < nq ? a + bs : nq;
+      int lo, hi;
+      g.key_range(a, b, &lo, &hi);
+      for (int j = 0; j < nk; ++j) {
+        bool any = false;
+        for (int i = a; i < b; ++i) any |= sees(mode, W, nk, i, j);
+        if (any) CHECK(lo <= j && j < hi, "key_range misses m%d W%d rows[%d,%d) j%d\n", mode, W, a, b, j);
+      }
+      // tight: the ends of a non-empty range are visible to some row
+      if (lo < hi) {
+        bool e0 = false, e1 = false;
+        for (int i = a; i < b; ++i) {
+          e0 |= sees(mode, W, nk, i, lo);
+          e1 |= sees(mode, W, nk, i, hi - 1);
+        }
+        CHECK(e0 && e1, "key_range loose m%d W%d rows[%d,%d) [%d,%d)\n", mode, W, a, b, lo, hi);
+      }
+      for (int j0 = 0; j0 < nk; j0 += bs) {
+        const int j1 = j0 + bs;
+        bool all = b <= nq && j1 <= nk;
+        for (int i = a; i < b && all; ++i)
+          for (int j = j0; j < j1 && all; ++j) all = sees(mode, W, nk, i, j);
+        CHECK(all == g.tile_full(a, b, j0, j1), "tile_full m%d W%d rows[%d,%d) keys[%d,%d)\n", mode, W,
+              a, b, j0, j1);
+      }
+    }
+    for (int a = 0; a < nk; a += bs) {
+      const int b = a + bs;
+      int lo, hi;
+      g.query_range(a, b, &lo, &hi);
+      for (int i = 0; i < nq; ++i) {
+        bool any = false;
+        for (int j = a; j < b && j < nk; ++j) any |= sees(mode, W, nk, i, j);
+        if (any) CHECK(lo <= i && i < hi, "query_range misses m%d W%d keys[%d,%d) i%d\n", mode, W, a, b, i);
+      }
+      if (lo < hi) {
+        bool e0 = false, e1 = false;
+        for (int j = a; j < b && j < nk; ++j) {
+          e0 |= sees(mode, W, nk, lo, j);
+          e1 |= sees(mode, W, nk, hi - 1, j);
+        }
+        CHECK(e0 && e1, "query_range loose m%d W%d keys[%d,%d) [%d,%d)\n", mode, W, a, b, lo, hi);
+      }
+    }
+  }
+}
+
+int main() {
+  const int sizes[] = {1, 2, 5, 16, 17, 33, 64, 65};
+  for (int nq : sizes)
+    for (int nk : sizes) {
+      check(attn::kNone, 0, nq, nk);
+      check(attn::kCausal, 0, nq, nk);
+      const int wins[] = {1, 2, 3, 16, 40, 100};
+      for (int W : wins) check(attn::kSliding, W, nq, nk);
+      if (nq == nk)
+        for (int W = 1; W <= nk; ++W)
+          if (nk % W == 0) check(attn::kBlock, W, nq, nk);
+    }
+  std::printf("%d failures\n", fails);
+  return fails ? 1 : 0;
+}

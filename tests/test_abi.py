@@ -1,0 +1,144 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/attn.h declares, and its argument validation returns the documented
+status codes (attn_check_* make no device call, so no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from head_attention_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, ALIAS, DEVICE, LAUNCH = range(8)
+BF16, FP32 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.lib_path()):
+        from head_attention_attn_amd.build import build
+        build()
+    return binding.load_library()
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    return sorted(set(re.findall(r"ATTN_API\s+[\w\s\*]+?\b(attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_workspace_size",
+                                         "attn_check_fwd", "attn_check_bwd", "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.lib_path()],
+                         capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(declared_symbols()) <= exported
+    # nothing else of ours leaks out of the shared object
+    assert not [s for s in exported if s.startswith("_ZN4attn")]
+
+
+def test_status_strings(lib):
+    names = ["ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_MISALIGNED",
+             "ATTN_ERR_WORKSPACE", "ATTN_ERR_ALIAS", "ATTN_ERR_DEVICE", "ATTN_ERR_LAUNCH"]
+    for code, name in enumerate(names):
+        assert lib.attn_status_string(code).decode() == name
+    assert lib.attn_status_string(99).decode() == "ATTN_ERR_UNKNOWN"
+
+
+def test_workspace_size(lib):
+    assert lib.attn_bwd_workspace_size(1, 1, 1) == 256
+    assert lib.attn_bwd_workspace_size(1, 20, 8192) == 20 * 8192 * 4
+    assert lib.attn_bwd_workspace_size(3, 1, 5) == 256
+    assert lib.attn_bwd_workspace_size(0, 1, 5) == 0
+
+
+# Fake, never-dereferenced device addresses, far apart and 16-byte aligned.
+BASE = 1 << 40
+STEP = 1 << 32
+
+
+def ptrs(n):
+    return [BASE + i * STEP for i in range(n)]
+
+
+def fwd_args(**kw):
+    a = dict(dtype=BF16, B=2, H=3, Nq=100, Nk=100, d=64, scale=0.125, mask=0, window=0)
+    q, k, v, o, lse = ptrs(5)
+    a.update(q=q, k=k, v=v, o=o, lse=lse)
+    a.update(kw)
+    return a
+
+
+def check_fwd(lib, **kw):
+    a = fwd_args(**kw)
+    return lib.attn_check_fwd(a["dtype"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                              a["mask"], a["window"], a["q"], a["k"], a["v"], a["o"], a["lse"])
+
+
+def check_bwd(lib, ws_bytes=None, **kw):
+    a = fwd_args(**kw)
+    p = ptrs(11)
+    names = ["q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"]
+    b = {n: p[i] for i, n in enumerate(names)}
+    b.update({k: v for k, v in kw.items() if k in names})
+    ws = lib.attn_bwd_workspace_size(a["B"], a["H"], a["Nq"]) if ws_bytes is None else ws_bytes
+    return lib.attn_check_bwd(a["dtype"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                              a["mask"], a["window"], b["q"], b["k"], b["v"], b["o"], b["lse"],
+                              b["dout"], b["dq"], b["dk"], b["dv"], b["ws"], ws)
+
+
+def test_valid_arguments_pass(lib):
+    for mask, window in ((0, 0), (1, 0), (2, 1024), (3, 4)):
+        assert check_fwd(lib, mask=mask, window=window) == OK
+        assert check_bwd(lib, mask=mask, window=window) == OK
+    assert check_fwd(lib, dtype=FP32, d=96) == OK
+    assert check_fwd(lib, Nq=7, Nk=300, mask=1) == OK          # Nq != Nk, top-left causal
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), UNSUPPORTED),
+    (dict(d=80), UNSUPPORTED),
+    (dict(d=256), UNSUPPORTED),
+    (dict(B=0), INVALID),
+    (dict(H=-1), INVALID),
+    (dict(Nq=0), INVALID),
+    (dict(Nk=0), INVALID),
+    (dict(mask=4), INVALID),
+    (dict(mask=-1), INVALID),
+    (dict(mask=2, window=0), INVALID),
+    (dict(mask=3, window=0), INVALID),
+    (dict(mask=3, window=7), INVALID),            # 100 % 7 != 0
+    (dict(mask=3, window=4, Nk=96), INVALID),     # block needs Nq == Nk
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(q=0), INVALID),
+    (dict(lse=0), INVALID),
+    (dict(k=BASE + 8), MISALIGNED),
+    (dict(o=BASE + 20 * STEP + 4), MISALIGNED),
+    (dict(o=BASE), ALIAS),                                   # output == input
+    (dict(lse=BASE + 3 * STEP + 1024), ALIAS),               # lse inside o
+    (dict(Nq=1 << 31), INVALID),
+])
+def test_fwd_validation(lib, kw, status):
+    assert check_fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0), WORKSPACE),
+    (dict(ws_bytes=16), WORKSPACE),
+    (dict(dq=BASE), ALIAS),
+    (dict(dv=BASE + 6 * STEP + 64), ALIAS),        # dv inside dq
+    (dict(ws=BASE + 5 * STEP), ALIAS),             # workspace on top of dout
+    (dict(dout=BASE + 5 * STEP + 2), MISALIGNED),
+    (dict(dk=0), INVALID),
+    (dict(d=48), UNSUPPORTED),
+])
+def test_bwd_validation(lib, kw, status):
+    assert check_bwd(lib, **kw) == status
