@@ -1,0 +1,358 @@
+"""Throughput of fused attention forward + backward on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already
+resident in HBM: ``attn_fwd`` (O and lse), then the three backward passes
+(row sums D, dK/dV, dQ) through ``attn_bwd_passes``, all on torch's current
+stream.  W untimed warmup steps, then K timed steps bracketed by a device
+synchronisation on both sides.  HIP events recorded between the calls give
+each kernel's average duration over the timed region.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value      algorithmic TFLOP/s of the step: (4 d + 10 d) flops per visible
+             (query, key) pair (forward 4 d, backward 10 d) over the step time
+  roofline   the kernel with the largest share of the step, its algorithmic
+             bytes (HBM-bound) or flops (MFMA-bound) per launch over its
+             measured average duration, against the MI355X peak; ``traffic``
+             is the HBM bytes per launch that rocprofv3 counters measured for
+             that kernel (profiles/traffic_<workload>.txt), or null when the
+             kernel sources changed since
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+             workload on this host, in the same unit
+  parity     GPU outputs of the sampled slices against the oracle, checked
+             outside the timed region
+
+Workloads (``--workload``): block_local_hiera (default; Hiera-Base mask-unit
+attention, 49 windows of 64 tokens, B=128, d=96), global_vision, causal_lm,
+sliding_pseudo_head, tiny_exact_fp32.  ``--gpus`` above 1 is refused: this
+path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+KERNELS = ("fwd", "rowsum", "dkdv", "dq")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ work accounting
+
+def row_intervals(mask: str, window: int, nq: int, nk: int):
+    """Visible key interval [lo, hi) of every query row (closed forms)."""
+    i = np.arange(nq, dtype=np.int64)
+    if mask == "none":
+        lo, hi = np.zeros_like(i), np.full_like(i, nk)
+    elif mask == "causal":
+        lo, hi = np.zeros_like(i), np.minimum(i + 1, nk)
+    elif mask == "sliding":
+        lo, hi = np.maximum(0, i - window + 1), np.minimum(i + 1, nk)
+    elif mask == "block":
+        lo = (i // window) * window
+        hi = np.minimum(lo + window, nk)
+    else:
+        raise ValueError(mask)
+    return lo, np.maximum(hi, lo)
+
+
+def visible_pairs(mask: str, window: int, nq: int, nk: int) -> int:
+    """Number of visible (query, key) pairs of one (batch, head)."""
+    lo, hi = row_intervals(mask, window, nq, nk)
+    return int((hi - lo).sum())
+
+
+def kernel_work(w, pairs_per_bh: int) -> dict:
+    """Algorithmic flops and compulsory HBM bytes per launch of each kernel.
+
+    flops per visible pair: fwd 4 d (Q K^T and P V); dK/dV pass 8 d (S, dP,
+    dV, dK); dQ pass 2 d (the dQ product; its recomputed S and dP are not
+    credited), so the backward totals 10 d.  Bytes: every tensor the kernel
+    must read or write, once."""
+    es = 2 if w.dtype == "bf16" else 4
+    bh = w.B * w.H
+    q_rows, k_rows, d = bh * w.Nq, bh * w.Nk, w.d
+    pairs = bh * pairs_per_bh
+    return {
+        "fwd": dict(flops=4 * d * pairs,
+                    bytes=(2 * q_rows * d + 2 * k_rows * d) * es + 4 * q_rows),
+        "rowsum": dict(flops=2 * d * q_rows, bytes=2 * q_rows * d * es + 4 * q_rows),
+        "dkdv": dict(flops=8 * d * pairs,
+                     bytes=(2 * q_rows * d + 4 * k_rows * d) * es + 8 * q_rows),
+        "dq": dict(flops=2 * d * pairs,
+                   bytes=(3 * q_rows * d + 2 * k_rows * d) * es + 8 * q_rows),
+    }
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources, to tell whether stored counter
+    readings still describe the kernels being timed."""
+    csrc = os.path.join(ROOT, "head_attention_attn_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from profiles/traffic_<workload>.txt when it was
+    taken from the current kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != source_digest():
+        return None
+    val = fields.get(f"traffic_bytes_per_launch.{kernel}")
+    return float(val) if val is not None else None
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(w, host_inputs, pairs_per_bh, budget_s: float, gpu_out):
+    """Time the fp64 oracle on whole (batch, head) slices, one at a time, until
+    about ``budget_s`` seconds are spent; compare those slices of the GPU
+    outputs with the oracle's while at it."""
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import oracle_bwd, oracle_fwd
+
+    q, k, v, do = host_inputs
+    flop_per_bh = 14 * w.d * pairs_per_bh
+    worst = {}
+    done, spent = 0, 0.0
+    tol = (2e-2, 5e-3) if w.dtype == "bf16" else (1e-5, 1e-5)
+    total_bh = w.B * w.H
+    # spread the sampled slices over the batch: first, last, then every 7th
+    # index, then the rest, until the time budget is spent
+    order = [0, total_bh - 1] + [i for r in range(7) for i in range(r, total_bh, 7)]
+    seen = []
+    for idx in order:
+        if idx in seen:
+            continue
+        seen.append(idx)
+        b, h = divmod(idx, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qs, ks, vs, dos = (t[sl].to(torch.float64).numpy() for t in (q, k, v, do))
+        t0 = time.perf_counter()
+        ro, rl = oracle_fwd(qs, ks, vs, w.scale, w.mask, w.window)
+        rdq, rdk, rdv = oracle_bwd(qs, ks, vs, dos, w.scale, w.mask, w.window)
+        spent += time.perf_counter() - t0
+        done += 1
+        for name, ref in (("O", ro), ("dQ", rdq), ("dK", rdk), ("dV", rdv)):
+            x = gpu_out[name][sl].double().numpy()
+            diff = x - ref
+            m = float(np.abs(diff).max())
+            r = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+            pm, pr = worst.get(name, (0.0, 0.0))
+            worst[name] = (max(pm, m), max(pr, r))
+        if spent >= budget_s:
+            break
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    base = {
+        "value": flop_per_bh * done / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} of {total_bh} (batch, head) slices of the same workload, "
+                   f"fwd+bwd, fp64 NumPy ({blas[0].get('internal_api', '?') if blas else '?'} "
+                   f"BLAS, {threads} threads; elementwise exp single-threaded), "
+                   f"{spent:.1f} s"),
+    }
+    ok = all(m <= tol[0] and r <= tol[1] for m, r in worst.values())
+    parity = {"slices": done, "pass": bool(ok),
+              "max_abs": {k: round(v[0], 6) for k, v in worst.items()},
+              "rel_l2": {k: round(v[1], 7) for k, v in worst.items()}}
+    return base, parity
+
+
+# --------------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="block_local_hiera")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU-oracle baseline (0 skips it)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run a plain device copy of this "
+                         "many MiB 5 times (a known-size reference for HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): "
+              "the attention path is not sharded across GPUs", file=sys.stderr)
+        return 2
+
+    import torch
+    import head_attention_attn_amd as attn
+    from head_attention_attn_amd.inputs import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] {w} on {props.name} ({getattr(props, 'gcnArchName', '?')}, "
+        f"{props.multi_processor_count} CUs)")
+
+    host = workload_inputs(w, seed=0)
+    q, k, v, do = (t.to(dev) for t in host)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(attn.binding.workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8,
+                     device=dev)
+    kw = dict(mask=w.mask, window=w.window, scale=w.scale)
+
+    def launch(kernel):
+        if kernel == "fwd":
+            attn.fwd(q, k, v, out=o, lse=lse, **kw)
+        else:
+            bit = {"rowsum": attn.binding.PASS_ROWSUM, "dkdv": attn.binding.PASS_DKDV,
+                   "dq": attn.binding.PASS_DQ}[kernel]
+            attn.bwd(q, k, v, o, lse, do, workspace=ws, dq=dq, dk=dk, dv=dv, passes=bit, **kw)
+
+    for _ in range(args.warmup):
+        for kn in KERNELS:
+            launch(kn)
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)]
+          for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    start.record()
+    for s in range(K):
+        ev[s][0].record()
+        for i, kn in enumerate(KERNELS):
+            launch(kn)
+            ev[s][i + 1].record()
+    stop.record()
+    torch.cuda.synchronize(dev)
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / K
+    kern_ms = {kn: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
+               for i, kn in enumerate(KERNELS)}
+    log(f"[bench] {ms_per_step:.4f} ms/step; per kernel (ms): "
+        + ", ".join(f"{kn} {kern_ms[kn]:.4f}" for kn in KERNELS))
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        log(f"[bench] copy calibration: 5 copies of {args.copy_calibration_mib} MiB")
+        del src, dst
+
+    # ---- accounting
+    pairs_bh = visible_pairs(w.mask, w.window, w.Nq, w.Nk)
+    pairs = pairs_bh * w.B * w.H
+    flops_step = 14 * w.d * pairs
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    work = kernel_work(w, pairs_bh)
+    dom = max(KERNELS, key=lambda kn: kern_ms[kn])
+    wk = work[dom]
+    ai = wk["flops"] / wk["bytes"]
+    if w.dtype == "bf16":
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        mfma_bound = ai >= ridge
+        peak_c, bound_c = MFMA_BF16_PEAK_TFLOPS, "mfma"
+    else:
+        ridge = FP32_VECTOR_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        mfma_bound = ai >= ridge
+        peak_c, bound_c = FP32_VECTOR_PEAK_TFLOPS, "alu"
+    t_dom = kern_ms[dom] * 1e-3
+    traffic = stored_traffic(w.name, dom)
+    if mfma_bound:
+        achieved = wk["flops"] / t_dom / 1e12
+        roof = {"bound": bound_c, "achieved": round(achieved, 2), "peak": peak_c,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_c, 4)}
+    else:
+        achieved = wk["bytes"] / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = {"flops": wk["flops"], "bytes": wk["bytes"]}
+
+    # ---- outputs for the parity check (a full fwd + bwd through attn_bwd)
+    o2, lse2 = attn.fwd(q, k, v, **kw)
+    dq2, dk2, dv2 = attn.bwd(q, k, v, o2, lse2, do, **kw)
+    torch.cuda.synchronize(dev)
+    same = all(torch.equal(a, b) for a, b in ((o, o2), (lse, lse2), (dq, dq2), (dk, dk2),
+                                              (dv, dv2)))
+    gpu_out = {"O": o2.cpu(), "dQ": dq2.cpu(), "dK": dk2.cpu(), "dV": dv2.cpu()}
+
+    cpu = None
+    parity = {"staged_equals_attn_bwd": bool(same)}
+    if args.cpu_seconds > 0:
+        log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        cpu, par = cpu_baseline(w, host, pairs_bh, args.cpu_seconds, gpu_out)
+        parity.update(par)
+
+    cfg = {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+           "mask": w.mask, "window": w.window, "dtype": w.dtype,
+           "visible_pairs": pairs, "step": "attn_fwd + attn_bwd (row sums, dK/dV, dQ)"}
+    rec = {
+        "metric": "attention fwd+bwd TFLOP/s at 1 MI355X; % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic i.i.d. N(0,1) Q, K, V, dO (seed 0), resident in HBM",
+        "config": cfg,
+        "pct_of_bf16_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 3),
+        "per_kernel_ms": {kn: round(kern_ms[kn], 5) for kn in KERNELS},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "cus": props.multi_processor_count, "torch": torch.__version__,
+                   "hip": torch.version.hip},
+    }
+    print(json.dumps(rec), flush=True)
+    ok = same and parity.get("pass", True)
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

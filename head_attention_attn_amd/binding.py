@@ -49,6 +49,8 @@ def load_library():
                              ctypes.c_int, i64, vp, vp, vp, vp, fp, vp, vp, vp, vp,
                              vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_passes.argtypes = [ctypes.c_int] + lib.attn_bwd.argtypes
+    lib.attn_bwd_passes.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_check_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_float,
@@ -109,9 +111,14 @@ def workspace_bytes(B: int, H: int, Nq: int) -> int:
     return int(load_library().attn_bwd_workspace_size(B, H, Nq))
 
 
+PASS_ROWSUM, PASS_DKDV, PASS_DQ, PASS_ALL = 1, 2, 4, 7
+
+
 def bwd(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
-        workspace=None, dq=None, dk=None, dv=None):
-    """dQ, dK, dV of attention given dO.  Returns tensors shaped like q, k, v."""
+        workspace=None, dq=None, dk=None, dv=None, passes: int = PASS_ALL):
+    """dQ, dK, dV of attention given dO.  Returns tensors shaped like q, k, v.
+    ``passes`` (a set of PASS_* bits) restricts the call to some of the
+    backward passes (``attn_bwd_passes``); the default runs all three."""
     lib = load_library()
     B, H, Nq, Nk, d = _geometry(q, k, v)
     if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, Nq):
@@ -122,11 +129,11 @@ def bwd(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib.attn_bwd(DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d),
+    st = lib.attn_bwd_passes(int(passes), DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d),
                       MASK_CODES[mask], int(window), q.data_ptr(), k.data_ptr(),
                       v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
                       workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd_passes")
     return dq, dk, dv

@@ -13,6 +13,11 @@
 #include "attn.h"
 #include "attn_common.hpp"
 
+static_assert(int(ATTN_PASS_ROWSUM) == int(attn::kPassRowSum) &&
+                  int(ATTN_PASS_DKDV) == int(attn::kPassDKDV) &&
+                  int(ATTN_PASS_DQ) == int(attn::kPassDQ) && int(ATTN_PASS_ALL) == int(attn::kPassAll),
+              "pass bits of attn.h and the launchers agree");
+
 namespace {
 
 constexpr int64_t kMaxSeq = int64_t(1) << 30;   // per-(b,h) row counts fit int32 math
@@ -170,10 +175,12 @@ int attn_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
   return err ? ATTN_ERR_LAUNCH : ATTN_OK;
 }
 
-int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
-             int mask, int64_t window, const void* q, const void* k, const void* v,
-             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-             void* workspace, size_t workspace_bytes, void* stream) {
+int attn_bwd_passes(int passes, int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                    int64_t d, float scale, int mask, int64_t window, const void* q,
+                    const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (passes < 1 || passes > ATTN_PASS_ALL) return ATTN_ERR_INVALID_ARG;
   int st = attn_check_bwd(dtype, B, H, Nq, Nk, d, scale, mask, window, q, k, v, o, lse, dout,
                           dq, dk, dv, workspace, workspace_bytes);
   if (st) return st;
@@ -197,9 +204,17 @@ int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
   a.scale = scale;
   a.mg = make_geom(mask, Nq, Nk, window);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int err = dtype == ATTN_BF16 ? attn::launch_bwd_bf16(a, (int)d, s)
-                                     : attn::launch_bwd_fp32(a, (int)d, s);
+  const int err = dtype == ATTN_BF16 ? attn::launch_bwd_bf16(a, (int)d, s, passes)
+                                     : attn::launch_bwd_fp32(a, (int)d, s, passes);
   return err ? ATTN_ERR_LAUNCH : ATTN_OK;
+}
+
+int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+             int mask, int64_t window, const void* q, const void* k, const void* v,
+             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd_passes(ATTN_PASS_ALL, dtype, B, H, Nq, Nk, d, scale, mask, window, q, k, v, o,
+                         lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -487,22 +487,28 @@ int launch_fwd_d(const FwdArgs& a, hipStream_t s) {
 }
 
 template <int D>
-int launch_bwd_d(const BwdArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.B * a.H * a.nq;
-  hipLaunchKernelGGL((dsum_bf16_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s,
-                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dsum, rows);
-  int err = (int)hipGetLastError();
-  if (err) return err;
+int launch_bwd_d(const BwdArgs& a, hipStream_t s, int passes) {
   constexpr int NW = 4;
-  const int nkt = (a.nk + 32 * NW - 1) / (32 * NW);
-  hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW>), dim3((unsigned)((int64_t)nkt * a.B * a.H)),
-                     dim3(NW * 64), 0, s, a, nkt);
-  err = (int)hipGetLastError();
-  if (err) return err;
-  const int nqt = (a.nq + 32 * NW - 1) / (32 * NW);
-  hipLaunchKernelGGL((dq_bf16_kernel<D, NW>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
-                     dim3(NW * 64), 0, s, a, nqt);
-  return (int)hipGetLastError();
+  int err = 0;
+  if (passes & kPassRowSum) {
+    const int64_t rows = (int64_t)a.B * a.H * a.nq;
+    hipLaunchKernelGGL((dsum_bf16_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                       s, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dsum, rows);
+    if ((err = (int)hipGetLastError())) return err;
+  }
+  if (passes & kPassDKDV) {
+    const int nkt = (a.nk + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW>), dim3((unsigned)((int64_t)nkt * a.B * a.H)),
+                       dim3(NW * 64), 0, s, a, nkt);
+    if ((err = (int)hipGetLastError())) return err;
+  }
+  if (passes & kPassDQ) {
+    const int nqt = (a.nq + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((dq_bf16_kernel<D, NW>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
+                       dim3(NW * 64), 0, s, a, nqt);
+    if ((err = (int)hipGetLastError())) return err;
+  }
+  return 0;
 }
 
 }  // namespace
@@ -516,11 +522,11 @@ int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
   return (int)hipErrorInvalidValue;
 }
 
-int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s) {
+int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s, int passes) {
   switch (d) {
-    case 64: return launch_bwd_d<64>(a, s);
-    case 96: return launch_bwd_d<96>(a, s);
-    case 128: return launch_bwd_d<128>(a, s);
+    case 64: return launch_bwd_d<64>(a, s, passes);
+    case 96: return launch_bwd_d<96>(a, s, passes);
+    case 128: return launch_bwd_d<128>(a, s, passes);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -113,15 +113,19 @@ struct BwdArgs {
   MaskGeom mg;
 };
 
+// backward pass bits (the values of include/attn.h's ATTN_PASS_*)
+enum BwdPass : int { kPassRowSum = 1, kPassDKDV = 2, kPassDQ = 4, kPassAll = 7 };
+
 }  // namespace attn
 
 #if defined(__HIPCC__)
 namespace attn {
 // Launchers, one per dtype; each picks its kernel instantiation from (d, mask).
-// They return the hipError_t of the launch(es) as an int.
+// They return the hipError_t of the launch(es) as an int.  `passes` is a set
+// of backward pass bits (row sums, dK/dV, dQ), launched in that order.
 int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
-int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s);
+int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s, int passes);
 int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s);
-int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s);
+int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s, int passes);
 }  // namespace attn
 #endif

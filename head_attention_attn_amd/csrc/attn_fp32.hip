@@ -171,17 +171,23 @@ int fwd_d(const FwdArgs& a, hipStream_t s) {
 }
 
 template <int D>
-int bwd_d(const BwdArgs& a, hipStream_t s) {
+int bwd_d(const BwdArgs& a, hipStream_t s, int passes) {
   const int64_t qrows = (int64_t)a.B * a.H * a.nq, krows = (int64_t)a.B * a.H * a.nk;
-  hipLaunchKernelGGL((dsum_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s,
-                     (const float*)a.o, (const float*)a.dout, a.dsum, qrows);
-  int err = (int)hipGetLastError();
-  if (err) return err;
-  hipLaunchKernelGGL((dkdv_fp32_kernel<D>), dim3(blocks_for(krows)), dim3(256), 0, s, a);
-  err = (int)hipGetLastError();
-  if (err) return err;
-  hipLaunchKernelGGL((dq_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s, a);
-  return (int)hipGetLastError();
+  int err = 0;
+  if (passes & kPassRowSum) {
+    hipLaunchKernelGGL((dsum_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s,
+                       (const float*)a.o, (const float*)a.dout, a.dsum, qrows);
+    if ((err = (int)hipGetLastError())) return err;
+  }
+  if (passes & kPassDKDV) {
+    hipLaunchKernelGGL((dkdv_fp32_kernel<D>), dim3(blocks_for(krows)), dim3(256), 0, s, a);
+    if ((err = (int)hipGetLastError())) return err;
+  }
+  if (passes & kPassDQ) {
+    hipLaunchKernelGGL((dq_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s, a);
+    if ((err = (int)hipGetLastError())) return err;
+  }
+  return 0;
 }
 
 }  // namespace
@@ -195,11 +201,11 @@ int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s) {
   return (int)hipErrorInvalidValue;
 }
 
-int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s) {
+int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s, int passes) {
   switch (d) {
-    case 64: return bwd_d<64>(a, s);
-    case 96: return bwd_d<96>(a, s);
-    case 128: return bwd_d<128>(a, s);
+    case 64: return bwd_d<64>(a, s, passes);
+    case 96: return bwd_d<96>(a, s, passes);
+    case 128: return bwd_d<128>(a, s, passes);
   }
   return (int)hipErrorInvalidValue;
 }

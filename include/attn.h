@@ -140,6 +140,39 @@ ATTN_API int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, i
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward pass bits for attn_bwd_passes.
+ *   ATTN_PASS_ROWSUM  D_i = sum_c dO[i][c] * O[i][c] into the workspace
+ *   ATTN_PASS_DKDV    dK and dV (reads the workspace's D)
+ *   ATTN_PASS_DQ      dQ        (reads the workspace's D)
+ */
+enum attn_pass {
+  ATTN_PASS_ROWSUM = 1,
+  ATTN_PASS_DKDV = 2,
+  ATTN_PASS_DQ = 4,
+  ATTN_PASS_ALL = 7
+};
+
+/*
+ * attn_bwd_passes -- attn_bwd restricted to the passes in the bit set
+ * `passes` (1..ATTN_PASS_ALL; anything else is ATTN_ERR_INVALID_ARG),
+ * enqueued in the order row sums, dK/dV, dQ.  attn_bwd is
+ * attn_bwd_passes(ATTN_PASS_ALL, ...).  Every argument is validated exactly
+ * as in attn_bwd, including the outputs a pass does not write.  The dK/dV
+ * and dQ passes read D from the workspace, so they need a row-sum pass with
+ * the same o, dout and workspace earlier in stream order; once that pass is
+ * done the two are independent of each other and a caller may enqueue them
+ * on two streams (with an event from the row-sum pass's stream).  Passing a
+ * workspace that holds no row sums gives wrong gradients, not a fault.  Use:
+ * overlapping the two passes, and timing each pass on its own.
+ */
+ATTN_API int attn_bwd_passes(int passes, int dtype, int64_t B, int64_t H, int64_t Nq,
+                             int64_t Nk, int64_t d, float scale, int mask, int64_t window,
+                             const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_check_fwd / attn_check_bwd -- the argument validation of attn_fwd /
  * attn_bwd alone: no device query, no launch.  Same arguments (the stream is
  * not needed).  Returns the status the entry point would return before

@@ -29,7 +29,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_workspace_size",
+    assert declared_symbols() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_passes",
+                                         "attn_bwd_workspace_size",
                                          "attn_check_fwd", "attn_check_bwd", "attn_status_string"])
 
 

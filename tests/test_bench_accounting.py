@@ -1,0 +1,52 @@
+"""The benchmark's work accounting, on the CPU: visible-pair counts from the
+closed-form row intervals against a count of the oracle's visibility matrix,
+and the per-workload pair counts the flop figures rest on."""
+import pytest
+
+import bench
+from head_attention_attn_amd.inputs import WORKLOADS
+from oracle import visible
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 1),
+                                         ("sliding", 7), ("sliding", 500), ("block", 1),
+                                         ("block", 8), ("block", 48)])
+@pytest.mark.parametrize("nq,nk", [(48, 48), (1, 1), (37, 100), (100, 37)])
+def test_visible_pairs_match_the_oracle_mask(mask, window, nq, nk):
+    if mask == "block" and (nq != nk or nk % window):
+        pytest.skip("block-local needs Nq == Nk divisible by the window")
+    assert bench.visible_pairs(mask, window, nq, nk) == int(visible(mask, window, nq, nk).sum())
+
+
+def test_workload_pair_counts():
+    """Per (batch, head) counts, by hand: 49 windows of 64^2; 196^2; the
+    causal triangle N(N+1)/2; the sliding band sum of min(i+1, 1024)."""
+    pc = {n: bench.visible_pairs(w.mask, w.window, w.Nq, w.Nk) for n, w in WORKLOADS.items()}
+    assert pc["block_local_hiera"] == 49 * 64 * 64
+    assert pc["global_vision"] == 196 * 196
+    assert pc["causal_lm"] == 8192 * 8193 // 2
+    assert pc["sliding_pseudo_head"] == 1024 * 1025 // 2 + (4096 - 1024) * 1024
+    assert pc["tiny_exact_fp32"] == 128 * 128
+
+
+def test_kernel_work_sums_to_the_step():
+    w = WORKLOADS["causal_lm"]
+    pairs = bench.visible_pairs(w.mask, w.window, w.Nq, w.Nk)
+    work = bench.kernel_work(w, pairs)
+    fl = work["fwd"]["flops"] + work["dkdv"]["flops"] + work["dq"]["flops"]
+    assert fl == 14 * w.d * pairs * w.B * w.H
+    # block-local dK/dV pass: Q, dO, K, V, dK, dV in bf16 plus lse and D in fp32
+    b = WORKLOADS["block_local_hiera"]
+    rows = b.B * b.H * b.Nq
+    assert bench.kernel_work(b, 49 * 64 * 64)["dkdv"]["bytes"] == rows * (6 * b.d * 2 + 8)
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    import sys
+    argv = sys.argv
+    sys.argv = ["bench.py", "--gpus", "2"]
+    try:
+        assert bench.main() == 2
+    finally:
+        sys.argv = argv
+    assert "one GPU" in capsys.readouterr().err
