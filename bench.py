@@ -83,7 +83,8 @@ def kernel_work(w, pairs_per_bh: int) -> dict:
 
     flops per visible pair: fwd 4 d (Q K^T and P V); dK/dV pass 8 d (S, dP,
     dV, dK); dQ pass 2 d (the dQ product; its recomputed S and dP are not
-    credited), so the backward totals 10 d.  Bytes: every tensor the kernel
+    credited), so the backward totals 10 d, which is also what the fused
+    single-tile backward is credited with.  Bytes: every tensor the kernel
     must read or write, once."""
     es = 2 if w.dtype == "bf16" else 4
     bh = w.B * w.H
@@ -97,6 +98,10 @@ def kernel_work(w, pairs_per_bh: int) -> dict:
                      bytes=(2 * q_rows * d + 4 * k_rows * d) * es + 8 * q_rows),
         "dq": dict(flops=2 * d * pairs,
                    bytes=(3 * q_rows * d + 2 * k_rows * d) * es + 8 * q_rows),
+        # the fused single-tile backward: reads Q, K, V, dO, lse, writes dQ,
+        # dK, dV (its row sums come from P and dP in-tile, O is not read)
+        "bwd": dict(flops=10 * d * pairs,
+                    bytes=(3 * q_rows * d + 4 * k_rows * d) * es + 4 * q_rows),
     }
 
 
@@ -233,29 +238,34 @@ def main() -> int:
                      device=dev)
     kw = dict(mask=w.mask, window=w.window, scale=w.scale)
 
+    fused = attn.binding.bwd_fused(q, k, v, mask=w.mask, window=w.window)
+    kernels = ("fwd", "bwd") if fused else KERNELS
+
     def launch(kernel):
         if kernel == "fwd":
             attn.fwd(q, k, v, out=o, lse=lse, **kw)
+        elif kernel == "bwd":
+            attn.bwd(q, k, v, o, lse, do, workspace=ws, dq=dq, dk=dk, dv=dv, **kw)
         else:
             bit = {"rowsum": attn.binding.PASS_ROWSUM, "dkdv": attn.binding.PASS_DKDV,
                    "dq": attn.binding.PASS_DQ}[kernel]
             attn.bwd(q, k, v, o, lse, do, workspace=ws, dq=dq, dk=dk, dv=dv, passes=bit, **kw)
 
     for _ in range(args.warmup):
-        for kn in KERNELS:
+        for kn in kernels:
             launch(kn)
     torch.cuda.synchronize(dev)
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
           for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     start.record()
     for s in range(K):
         ev[s][0].record()
-        for i, kn in enumerate(KERNELS):
+        for i, kn in enumerate(kernels):
             launch(kn)
             ev[s][i + 1].record()
     stop.record()
@@ -263,9 +273,9 @@ def main() -> int:
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / K
     kern_ms = {kn: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
-               for i, kn in enumerate(KERNELS)}
+               for i, kn in enumerate(kernels)}
     log(f"[bench] {ms_per_step:.4f} ms/step; per kernel (ms): "
-        + ", ".join(f"{kn} {kern_ms[kn]:.4f}" for kn in KERNELS))
+        + ", ".join(f"{kn} {kern_ms[kn]:.4f}" for kn in kernels))
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -283,7 +293,7 @@ def main() -> int:
     flops_step = 14 * w.d * pairs
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     work = kernel_work(w, pairs_bh)
-    dom = max(KERNELS, key=lambda kn: kern_ms[kn])
+    dom = max(kernels, key=lambda kn: kern_ms[kn])
     wk = work[dom]
     ai = wk["flops"] / wk["bytes"]
     if w.dtype == "bf16":
@@ -325,7 +335,9 @@ def main() -> int:
 
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
            "mask": w.mask, "window": w.window, "dtype": w.dtype,
-           "visible_pairs": pairs, "step": "attn_fwd + attn_bwd (row sums, dK/dV, dQ)"}
+           "visible_pairs": pairs,
+           "step": ("attn_fwd + attn_bwd (one fused kernel: dK/dV and dQ waves side by side)"
+                    if fused else "attn_fwd + attn_bwd (row sums, dK/dV, dQ passes)")}
     rec = {
         "metric": "attention fwd+bwd TFLOP/s at 1 MI355X; % of bf16 MFMA peak",
         "value": round(value, 3),
@@ -341,7 +353,7 @@ def main() -> int:
         "data": "synthetic i.i.d. N(0,1) Q, K, V, dO (seed 0), resident in HBM",
         "config": cfg,
         "pct_of_bf16_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 3),
-        "per_kernel_ms": {kn: round(kern_ms[kn], 5) for kn in KERNELS},
+        "per_kernel_ms": {kn: round(kern_ms[kn], 5) for kn in kernels},
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,

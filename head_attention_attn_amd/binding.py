@@ -51,6 +51,8 @@ def load_library():
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_passes.argtypes = [ctypes.c_int] + lib.attn_bwd.argtypes
     lib.attn_bwd_passes.restype = ctypes.c_int
+    lib.attn_bwd_fused.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int, i64]
+    lib.attn_bwd_fused.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_check_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_float,
@@ -105,6 +107,14 @@ def fwd(q, k, v, mask: str = "none", window: int = 0, scale=None, out=None, lse=
     if st != 0:
         raise AttnError(st, "attn_fwd")
     return o, lse
+
+
+def bwd_fused(q, k, v, mask: str = "none", window: int = 0) -> bool:
+    """True when ``bwd`` runs as one fused kernel for these tensors (then
+    ``passes`` must be PASS_ALL)."""
+    B, H, Nq, Nk, d = _geometry(q, k, v)
+    return load_library().attn_bwd_fused(DTYPE_CODES[q.dtype], B, H, Nq, Nk, d,
+                                         MASK_CODES[mask], int(window)) == 1
 
 
 def workspace_bytes(B: int, H: int, Nq: int) -> int:

@@ -150,6 +150,13 @@ int attn_check_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int6
 
 size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq) { return ws_size(B, H, Nq); }
 
+int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int mask,
+                   int64_t window) {
+  if (check_geometry(dtype, B, H, Nq, Nk, d, 1.0f, mask, window) != ATTN_OK) return 0;
+  if (dtype != ATTN_BF16) return 0;
+  return make_geom(mask, Nq, Nk, window).local64() ? 1 : 0;
+}
+
 int attn_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
              int mask, int64_t window, const void* q, const void* k, const void* v, void* o,
              float* lse, void* stream) {
@@ -181,6 +188,8 @@ int attn_bwd_passes(int passes, int dtype, int64_t B, int64_t H, int64_t Nq, int
                     const void* dout, void* dq, void* dk, void* dv, void* workspace,
                     size_t workspace_bytes, void* stream) {
   if (passes < 1 || passes > ATTN_PASS_ALL) return ATTN_ERR_INVALID_ARG;
+  if (passes != ATTN_PASS_ALL && attn_bwd_fused(dtype, B, H, Nq, Nk, d, mask, window) == 1)
+    return ATTN_ERR_UNSUPPORTED;
   int st = attn_check_bwd(dtype, B, H, Nq, Nk, d, scale, mask, window, q, k, v, o, lse, dout,
                           dq, dk, dv, workspace, workspace_bytes);
   if (st) return st;

@@ -27,72 +27,11 @@
 //   dQ:    workgroup per block of 32*NW queries; loops over visible 64-key
 //          tiles:  S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 #include "attn_common.hpp"
-#include "mfma.hpp"
+#include "bf16_tile.hpp"
 
 namespace attn {
 
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.69314718055994531f;
-
-// Cooperative global -> register -> LDS staging of a ROWS x D bf16 tile whose
-// rows start at r0 of a [n][D] matrix; rows >= n read as zero.
-template <int ROWS, int D, int NT>
-struct TileLoader {
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int TOTAL = ROWS * CPR;
-  static constexpr int CH = (TOTAL + NT - 1) / NT;    // chunks per thread
-  uint4 r[CH];
-
-  __device__ __forceinline__ void load(const uint16_t* src, int r0, int n, int tid) {
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int gr = r0 + row;
-      r[t] = (c < TOTAL && gr < n)
-                 ? *reinterpret_cast<const uint4*>(src + (int64_t)gr * D + col)
-                 : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int stride, int tid) const {
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      if (c < TOTAL) *reinterpret_cast<uint4*>(lds + row * stride + col) = r[t];
-    }
-  }
-};
-
-template <int D>
-__device__ __forceinline__ void load_operand_rows(bf16x8 (&op)[D / 16], const uint16_t* rowp,
-                                                  bool valid, int gq) {
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    if (valid) {
-      op[kc] = *reinterpret_cast<const bf16x8*>(rowp + 16 * kc + 8 * gq);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) op[kc][s] = (__bf16)0.0f;
-    }
-  }
-}
-
-// Store a transposed 32-column accumulator block set (columns = this lane's
-// row of the output, rows = d) as bf16: d = 32*db + 8*i + 4*gq + j.
-template <int D>
-__device__ __forceinline__ void store_row_bf16(uint16_t* rowp, const f32x16 (&acc)[D / 32],
-                                               float mul, int gq) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint2*>(rowp + 32 * db + 8 * i + 4 * gq) =
-          pack_bf16x4(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul,
-                      acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
-}
 
 // ------------------------------------------------------------------ forward
 
@@ -514,6 +453,7 @@ int launch_bwd_d(const BwdArgs& a, hipStream_t s, int passes) {
 }  // namespace
 
 int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
+  if (a.mg.local64()) return launch_fwd_bf16_local(a, d, s);
   switch (d) {
     case 64: return launch_fwd_d<64>(a, s);
     case 96: return launch_fwd_d<96>(a, s);
@@ -523,6 +463,11 @@ int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
 }
 
 int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s, int passes) {
+  if (a.mg.local64()) {
+    // one fused kernel writes dQ, dK and dV; it takes no partial pass set
+    if (passes != kPassAll) return (int)hipErrorInvalidValue;
+    return launch_bwd_bf16_local(a, d, s);
+  }
   switch (d) {
     case 64: return launch_bwd_d<64>(a, s, passes);
     case 96: return launch_bwd_d<96>(a, s, passes);

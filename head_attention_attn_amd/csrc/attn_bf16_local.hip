@@ -1,0 +1,320 @@
+// attn_bf16_local.hip -- bf16 kernels for attention whose every query row sees
+// keys of its own 64-row tile only: block-local (mask-unit) attention with a
+// window that divides 64 ("hiera-optim 0.1.0" sdist, mask_unit.py,
+// MaskUnitAttentionFast: tokens split into independent windows, dense softmax
+// attention inside each window).  Such attention is HBM-bound: a 64-token
+// window with d = 96 costs ~4 MFLOP of MFMA work against ~100 KB of HBM
+// traffic, so these kernels are built around moving each byte once.
+//
+// Forward: one workgroup (2 waves) per 64-row tile.  K and V of the tile go
+// to LDS, each wave keeps 32 query rows as the register operand, and the
+// scores of a row are complete after one tile, so the softmax is a plain one
+// (exact row max, no rescaling).  Computed transposed like the general
+// forward kernel: S^T = K Q^T, O^T = V^T P^T with bf16 MFMA 32x32x16.
+//
+// Backward: one workgroup (4 waves) per 64-row tile, Q, K, V and dO staged in
+// LDS once.  The dK/dV pass and the dQ pass ("IHA-CUDA", Repository
+// Structure: separate backward kernels, no atomic accumulation here) run side
+// by side on different waves of the same workgroup: waves 0-1 own 32 keys
+// each (dV^T += dO^T P, dK^T += Q^T dS), waves 2-3 own 32 queries each
+// (dQ^T += K^T dS^T).  Because the tile holds every key a query row can see,
+// the row sums D_i = sum_j P_ij dP_ij (equal to sum_c dO_ic O_ic, the
+// "dPsum" of the backward pre-pass) are taken by the dQ waves from their own
+// P and dP and handed to the dK/dV waves through LDS: O is never read and the
+// backward makes one pass over HBM.
+#include "attn_common.hpp"
+#include "bf16_tile.hpp"
+
+namespace attn {
+
+namespace {
+
+constexpr int kTile = 64;
+
+// visibility inside a tile: rows and keys share a window (window = 1 << wshift
+// divides 64, so windows never cross tiles); a row >= n sees nothing and
+// every key of a row < n's window is < n (n is a multiple of the window).
+__device__ __forceinline__ bool local_vis(int qi, int kj, int n, int wshift) {
+  return qi < n && (qi >> wshift) == (kj >> wshift);
+}
+
+// ------------------------------------------------------------------ forward
+
+template <int D>
+__global__ __launch_bounds__(128) void fwd_local_kernel(FwdArgs a, int ntile, int wshift) {
+  constexpr int NT = 128, STR = D + 8, KC = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kTile * STR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int bh = blockIdx.x / ntile;
+  const int t0 = (blockIdx.x % ntile) * kTile;
+  const int n = a.nq;
+
+  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * n * D;
+  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * n * D;
+  const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * n * D;
+
+  TileLoader<kTile, D, NT> kt, vt;
+  kt.load(K, t0, n, tid);
+  vt.load(V, t0, n, tid);
+  const int myq = t0 + wave * 32 + (lane & 31);
+  const bool qvalid = myq < n;
+  bf16x8 qop[KC];
+  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
+  kt.store(sK, STR, tid);
+  vt.store(sV, STR, tid);
+  __syncthreads();
+
+  f32x16 s[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    s[mb] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      s[mb] = mfma32(lds_read8(sK + (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq), qop[kc],
+                     s[mb]);
+  }
+  const bool full = wshift == 6 && t0 + kTile <= n;
+  const float sl2 = a.scale * kLog2e;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float x = s[mb][e] * sl2;
+      if (!full) {
+        const int key = t0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+        if (!local_vis(myq, key, n, wshift)) x = -INFINITY;
+      }
+      s[mb][e] = x;
+      mx = fmaxf(mx, x);
+    }
+  mx = fmaxf(mx, xor32(mx));
+  const float mb2 = qvalid ? mx : 0.f;  // row max of the scaled scores, log2 units
+  float l = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = fast_exp2(s[mb][e] - mb2);
+      s[mb][e] = p;
+      l += p;
+    }
+  l += xor32(l);
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < kTile / 16; ++c) {
+    const bf16x8 pop = acc_chunk(s[c >> 1], c & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      oacc[db] = mfma32(lds_read_tr8(sV, STR, 16 * c, 32 * db, lane), pop, oacc[db]);
+  }
+  if (qvalid) {
+    store_row_bf16<D>((uint16_t*)a.o + ((int64_t)bh * n + myq) * D, oacc, 1.f / l, gq);
+    if (gq == 0) a.lse[(int64_t)bh * n + myq] = (mb2 + log2f(l)) * kLn2;
+  }
+}
+
+// ----------------------------------------------------------------- backward
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, int wshift) {
+  constexpr int NT = 256, STR = D + 8, KC = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kTile * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kTile * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[kTile * STR];  // dO
+  __shared__ __attribute__((aligned(16))) float sL[kTile];           // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[kTile];           // D_i
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int bh = blockIdx.x / ntile;
+  const int t0 = (blockIdx.x % ntile) * kTile;
+  const int n = a.nq;
+  const int64_t base = (int64_t)bh * n * D;
+
+  {
+    TileLoader<kTile, D, NT> lq, lk, lv, lg;
+    lq.load((const uint16_t*)a.q + base, t0, n, tid);
+    lk.load((const uint16_t*)a.k + base, t0, n, tid);
+    lv.load((const uint16_t*)a.v + base, t0, n, tid);
+    lg.load((const uint16_t*)a.dout + base, t0, n, tid);
+    if (tid < kTile) {
+      const int r = t0 + tid;
+      sL[tid] = r < n ? a.lse[(int64_t)bh * n + r] * kLog2e : 0.f;
+    }
+    lq.store(sQ, STR, tid);
+    lk.store(sK, STR, tid);
+    lv.store(sV, STR, tid);
+    lg.store(sG, STR, tid);
+  }
+  __syncthreads();
+
+  const float sl2 = a.scale * kLog2e;
+  const bool full = wshift == 6 && t0 + kTile <= n;
+  const bool dq_wave = wave >= 2;
+  const int own = 32 * (wave & 1) + (lane & 31);  // this lane's key (dK/dV) or query (dQ) in the tile
+
+  // dK/dV waves: x[qt] = P, y[qt] = dP for query rows 32 qt + ..., lane = key.
+  // dQ waves:    x[mb] = P^T, y[mb] = dP^T for keys 32 mb + ..., lane = query.
+  f32x16 x[2], y[2];
+  f32x16 acc0[DB], acc1[DB];  // dK^T, dV^T (dK/dV waves) or dQ^T (dQ waves, acc0)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    acc0[db] = f32x16{};
+    acc1[db] = f32x16{};
+  }
+
+  if (dq_wave) {
+    const int qi = t0 + own;
+    const float lse2 = sL[own];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      x[mb] = f32x16{};
+      y[mb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int kr = (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq;
+        const int qr = own * STR + 16 * kc + 8 * gq;
+        x[mb] = mfma32(lds_read8(sK + kr), lds_read8(sQ + qr), x[mb]);
+        y[mb] = mfma32(lds_read8(sV + kr), lds_read8(sG + qr), y[mb]);
+      }
+    }
+    float dsum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = t0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+        const bool vis = full || local_vis(qi, key, n, wshift);
+        const float p = vis ? fast_exp2(fmaf(x[mb][e], sl2, -lse2)) : 0.f;
+        x[mb][e] = p;
+        dsum = fmaf(p, y[mb][e], dsum);
+      }
+    dsum += xor32(dsum);
+    if (gq == 0) sD[own] = dsum;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[mb][e] = x[mb][e] * (y[mb][e] - dsum);
+  } else {
+    const int kj = t0 + own;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      x[qt] = f32x16{};
+      y[qt] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int qr = (qt * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq;
+        const int kr = own * STR + 16 * kc + 8 * gq;
+        x[qt] = mfma32(lds_read8(sQ + qr), lds_read8(sK + kr), x[qt]);
+        y[qt] = mfma32(lds_read8(sG + qr), lds_read8(sV + kr), y[qt]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[32 * qt + 8 * i + 4 * gq]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * i + j;
+          const int qi = t0 + 32 * qt + 8 * i + 4 * gq + j;
+          const bool vis = full || local_vis(qi, kj, n, wshift);
+          x[qt][e] = vis ? fast_exp2(fmaf(x[qt][e], sl2, -L4[j])) : 0.f;
+        }
+      }
+      // dV^T += dO^T P over this tile's 32 query rows
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pop = acc_chunk(x[qt], c);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc1[db] = mfma32(lds_read_tr8(sG, STR, 32 * qt + 16 * c, 32 * db, lane), pop, acc1[db]);
+      }
+    }
+  }
+
+  __syncthreads();  // sD complete
+
+  if (dq_wave) {
+    // dQ^T += K^T dS^T over the tile's 64 keys
+#pragma unroll
+    for (int c = 0; c < kTile / 16; ++c) {
+      const bf16x8 dsop = acc_chunk(x[c >> 1], c & 1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc0[db] = mfma32(lds_read_tr8(sK, STR, 16 * c, 32 * db, lane), dsop, acc0[db]);
+    }
+    const int qi = t0 + own;
+    if (qi < n) store_row_bf16<D>((uint16_t*)a.dq + base + (int64_t)qi * D, acc0, a.scale, gq);
+  } else {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[32 * qt + 8 * i + 4 * gq]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[qt][4 * i + j] *= (y[qt][4 * i + j] - D4[j]);
+      }
+      // dK^T += Q^T dS over this tile's 32 query rows
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 dsop = acc_chunk(x[qt], c);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc0[db] = mfma32(lds_read_tr8(sQ, STR, 32 * qt + 16 * c, 32 * db, lane), dsop, acc0[db]);
+      }
+    }
+    const int kj = t0 + own;
+    if (kj < n) {
+      store_row_bf16<D>((uint16_t*)a.dk + base + (int64_t)kj * D, acc0, a.scale, gq);
+      store_row_bf16<D>((uint16_t*)a.dv + base + (int64_t)kj * D, acc1, 1.f, gq);
+    }
+  }
+}
+
+int shift_of(int w) {
+  int s = 0;
+  while ((1 << s) < w) ++s;
+  return s;
+}
+
+template <int D>
+int fwd_d(const FwdArgs& a, hipStream_t s) {
+  const int ntile = (a.nq + kTile - 1) / kTile;
+  hipLaunchKernelGGL((fwd_local_kernel<D>), dim3((unsigned)((int64_t)ntile * a.B * a.H)),
+                     dim3(128), 0, s, a, ntile, shift_of(a.mg.window));
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int bwd_d(const BwdArgs& a, hipStream_t s) {
+  const int ntile = (a.nq + kTile - 1) / kTile;
+  hipLaunchKernelGGL((bwd_local_kernel<D>), dim3((unsigned)((int64_t)ntile * a.B * a.H)),
+                     dim3(256), 0, s, a, ntile, shift_of(a.mg.window));
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_fwd_bf16_local(const FwdArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return fwd_d<64>(a, s);
+    case 96: return fwd_d<96>(a, s);
+    case 128: return fwd_d<128>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_bwd_bf16_local(const BwdArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return bwd_d<64>(a, s);
+    case 96: return bwd_d<96>(a, s);
+    case 128: return bwd_d<128>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -77,6 +77,9 @@ struct MaskGeom {
     *hi = col_hi(imin(b, nk) - 1);
     if (a >= nk) *hi = *lo;
   }
+  // every query row sees only keys of its own 64-row tile (block-local with a
+  // window dividing 64; Nq == Nk is guaranteed for block-local)
+  ATTN_HD bool local64() const { return mode == kBlock && window >= 1 && 64 % window == 0; }
   // every (row, key) of rows [a, b) x keys [j0, j1) visible; needs b <= nq, j1 <= nk
   ATTN_HD bool tile_full(int a, int b, int j0, int j1) const {
     if (b > nq || j1 > nk) return false;
@@ -126,6 +129,9 @@ namespace attn {
 int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
 int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s, int passes);
 int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s);
+// single-tile bf16 kernels for MaskGeom::local64() (forward; fused backward)
+int launch_fwd_bf16_local(const FwdArgs& a, int d, hipStream_t s);
+int launch_bwd_bf16_local(const BwdArgs& a, int d, hipStream_t s);
 int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s, int passes);
 }  // namespace attn
 #endif

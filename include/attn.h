@@ -153,9 +153,24 @@ enum attn_pass {
 };
 
 /*
+ * attn_bwd_fused -- 1 when attn_bwd runs as ONE fused kernel for these
+ * arguments, else 0 (also 0 for arguments attn_bwd would reject).  Fused:
+ * bf16 block-local attention whose window divides 64, where every query row
+ * sees keys of its own 64-row tile only ("hiera-optim 0.1.0" sdist,
+ * mask_unit.py: mask-unit windows as independent dense attentions).  One
+ * workgroup then holds a whole tile: its dK/dV waves and its dQ waves run the
+ * two backward passes side by side, the row sums D_i are formed in-tile as
+ * sum_j P_ij dP_ij, the workspace is not used and O is not read.  In the
+ * fused case attn_bwd_passes accepts only ATTN_PASS_ALL.
+ */
+ATTN_API int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                            int mask, int64_t window);
+
+/*
  * attn_bwd_passes -- attn_bwd restricted to the passes in the bit set
  * `passes` (1..ATTN_PASS_ALL; anything else is ATTN_ERR_INVALID_ARG),
- * enqueued in the order row sums, dK/dV, dQ.  attn_bwd is
+ * enqueued in the order row sums, dK/dV, dQ.  Where attn_bwd_fused() is 1,
+ * any set but ATTN_PASS_ALL is ATTN_ERR_UNSUPPORTED.  attn_bwd is
  * attn_bwd_passes(ATTN_PASS_ALL, ...).  Every argument is validated exactly
  * as in attn_bwd, including the outputs a pass does not write.  The dK/dV
  * and dQ passes read D from the workspace, so they need a row-sum pass with

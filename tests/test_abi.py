@@ -29,7 +29,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_passes",
+    assert declared_symbols() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_passes", "attn_bwd_fused",
                                          "attn_bwd_workspace_size",
                                          "attn_check_fwd", "attn_check_bwd", "attn_status_string"])
 
@@ -143,3 +143,18 @@ def test_fwd_validation(lib, kw, status):
 ])
 def test_bwd_validation(lib, kw, status):
     assert check_bwd(lib, **kw) == status
+
+
+def test_fused_backward_predicate(lib):
+    """The backward is one fused kernel exactly for bf16 block-local attention
+    whose window divides 64; invalid geometry reports 0."""
+    f = lambda dtype, n, mask, w, d=96: lib.attn_bwd_fused(dtype, 2, 1, n, n, d, mask, w)
+    for w in (1, 2, 4, 8, 16, 32, 64):
+        assert f(BF16, 3136, 3, w) == 1
+    assert f(BF16, 3136, 3, 7 * 64) == 0        # window 448 > 64
+    assert f(BF16, 192, 3, 48) == 0             # 48 does not divide 64
+    assert f(FP32, 3136, 3, 64) == 0            # fp32 path is not fused
+    assert f(BF16, 3136, 0, 64) == 0            # mask none
+    assert f(BF16, 3136, 2, 64) == 0            # sliding
+    assert f(BF16, 100, 3, 64) == 0             # 100 % 64 != 0: invalid geometry
+    assert f(BF16, 128, 3, 64, d=80) == 0       # unsupported d

@@ -50,3 +50,13 @@ def test_more_than_one_gpu_is_refused(capsys):
     finally:
         sys.argv = argv
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_fused_backward_bytes():
+    """Fused block-local backward: Q, dO, K, V read, dQ, dK, dV written (bf16)
+    plus lse (fp32); 10 d flops per visible pair."""
+    b = WORKLOADS["block_local_hiera"]
+    rows = b.B * b.H * b.Nq
+    wk = bench.kernel_work(b, 49 * 64 * 64)["bwd"]
+    assert wk["bytes"] == rows * (7 * b.d * 2 + 4)
+    assert wk["flops"] == 10 * b.d * 49 * 64 * 64 * b.B * b.H

@@ -173,3 +173,29 @@ def test_error_paths_leave_outputs_untouched():
     assert ei.value.status == 5
     torch.cuda.synchronize()
     assert bool((o == 7).all()) and bool((lse == 7).all())
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("window,n", [(64, 192), (32, 96), (16, 208), (8, 40), (4, 12), (2, 130),
+                                      (1, 65)])
+def test_block_local_single_tile_path(d, window, n):
+    """Block-local windows dividing 64 take the single-tile kernels (fused
+    backward); n not a multiple of 64 leaves a partial last tile.
+
+    With windows of 1-4 keys the softmax barely averages, so dV (a sum of up
+    to w rows of dO) reaches |5|, where the bf16 rounding of the output alone
+    is up to 2^-8 * |x| = 0.02: the max-abs bound grows by 2^-8 * max|ref|
+    for those windows.  rel-L2 keeps the 5e-3 bound."""
+    B, H = 3, 2
+    q, k, v, _ = make_inputs(B, H, n, n, d, "bf16", seed=10)
+    assert attn.binding.bwd_fused(q.cuda(), k.cuda(), v.cuda(), mask="block", window=window)
+    parity_case(B, H, n, n, d, "bf16", "block", window, seed=10,
+                amax_rel=2.0 ** -8 if window <= 4 else 0.0)
+
+
+def test_fused_backward_rejects_partial_pass_sets():
+    q, k, v, do = (t.cuda() for t in make_inputs(1, 1, 128, 128, 96, "bf16", seed=11))
+    o, lse = attn.fwd(q, k, v, mask="block", window=64)
+    with pytest.raises(attn.AttnError) as ei:
+        attn.bwd(q, k, v, o, lse, do, mask="block", window=64, passes=attn.binding.PASS_DKDV)
+    assert ei.value.status == 2
