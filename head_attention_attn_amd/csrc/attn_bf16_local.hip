@@ -41,7 +41,7 @@ __device__ __forceinline__ bool local_vis(int qi, int kj, int n, int wshift) {
 // ------------------------------------------------------------------ forward
 
 template <int D>
-__global__ __launch_bounds__(128) void fwd_local_kernel(FwdArgs a, int ntile, int wshift) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int wshift) {
   constexpr int NT = 128, STR = D + 8, KC = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * STR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kTile * STR];
@@ -113,10 +113,13 @@ __global__ __launch_bounds__(128) void fwd_local_kernel(FwdArgs a, int ntile, in
     for (int db = 0; db < DB; ++db)
       oacc[db] = mfma32(lds_read_tr8(sV, STR, 16 * c, 32 * db, lane), pop, oacc[db]);
   }
-  if (qvalid) {
-    store_row_bf16<D>((uint16_t*)a.o + ((int64_t)bh * n + myq) * D, oacc, 1.f / l, gq);
-    if (gq == 0) a.lse[(int64_t)bh * n + myq] = (mb2 + log2f(l)) * kLn2;
-  }
+  // O rows through LDS (sK is free once every wave is past its products) so
+  // that the global stores are whole rows, 16 bytes per lane
+  __syncthreads();
+  acc_to_lds<D>(sK, STR, wave * 32 + (lane & 31), oacc, qvalid ? 1.f / l : 0.f, gq);
+  if (qvalid && gq == 0) a.lse[(int64_t)bh * n + myq] = (mb2 + log2f(l)) * kLn2;
+  __syncthreads();
+  store_tile<kTile, D, NT>((uint16_t*)a.o + (int64_t)bh * n * D, t0, n, sK, STR, tid);
 }
 
 // ----------------------------------------------------------------- backward
@@ -247,8 +250,6 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
       for (int db = 0; db < DB; ++db)
         acc0[db] = mfma32(lds_read_tr8(sK, STR, 16 * c, 32 * db, lane), dsop, acc0[db]);
     }
-    const int qi = t0 + own;
-    if (qi < n) store_row_bf16<D>((uint16_t*)a.dq + base + (int64_t)qi * D, acc0, a.scale, gq);
   } else {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -258,7 +259,6 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[qt][4 * i + j] *= (y[qt][4 * i + j] - D4[j]);
       }
-      // dK^T += Q^T dS over this tile's 32 query rows
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 dsop = acc_chunk(x[qt], c);
@@ -267,12 +267,18 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
           acc0[db] = mfma32(lds_read_tr8(sQ, STR, 32 * qt + 16 * c, 32 * db, lane), dsop, acc0[db]);
       }
     }
-    const int kj = t0 + own;
-    if (kj < n) {
-      store_row_bf16<D>((uint16_t*)a.dk + base + (int64_t)kj * D, acc0, a.scale, gq);
-      store_row_bf16<D>((uint16_t*)a.dv + base + (int64_t)kj * D, acc1, 1.f, gq);
-    }
   }
+  __syncthreads();
+  if (dq_wave) {
+    acc_to_lds<D>(sQ, STR, own, acc0, a.scale, gq);
+  } else {
+    acc_to_lds<D>(sK, STR, own, acc0, a.scale, gq);
+    acc_to_lds<D>(sV, STR, own, acc1, 1.f, gq);
+  }
+  __syncthreads();
+  store_tile<kTile, D, NT>((uint16_t*)a.dq + base, t0, n, sQ, STR, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.dk + base, t0, n, sK, STR, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.dv + base, t0, n, sV, STR, tid);
 }
 
 int shift_of(int w) {

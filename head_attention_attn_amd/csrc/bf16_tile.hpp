@@ -70,5 +70,41 @@ __device__ __forceinline__ void store_row_bf16(uint16_t* rowp, const f32x16 (&ac
                       acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
 }
 
+// Write a transposed accumulator set (rows = d, this lane's column = output
+// row `row` of an LDS tile) into the LDS tile as bf16, scaled by `mul`:
+// element (row, 32*db + 8*i + 4*gq + j).  Used to turn per-lane output rows
+// into a row-major tile that TileStorer writes out with coalesced 16-byte
+// stores (a direct store of one row per lane would scatter 8-byte pieces over
+// 32 rows per instruction).
+template <int D>
+__device__ __forceinline__ void acc_to_lds(uint16_t* tile, int stride, int row,
+                                           const f32x16 (&acc)[D / 32], float mul, int gq) {
+  uint16_t* rp = tile + row * stride;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint2*>(rp + 32 * db + 8 * i + 4 * gq) =
+          pack_bf16x4(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul,
+                      acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
+}
+
+// Cooperative LDS -> global copy of a ROWS x D bf16 tile to rows r0.. of a
+// [n][D] matrix, 16 bytes per lane per step, consecutive lanes on
+// consecutive addresses; rows >= n are not written.
+template <int ROWS, int D, int NT>
+__device__ __forceinline__ void store_tile(uint16_t* dst, int r0, int n, const uint16_t* lds,
+                                           int stride, int tid) {
+  constexpr int CPR = D / 8, TOTAL = ROWS * CPR, CH = (TOTAL + NT - 1) / NT;
+#pragma unroll
+  for (int t = 0; t < CH; ++t) {
+    const int c = tid + t * NT;
+    const int row = c / CPR, col = (c % CPR) * 8;
+    if (c < TOTAL && r0 + row < n)
+      *reinterpret_cast<uint4*>(dst + (int64_t)(r0 + row) * D + col) =
+          *reinterpret_cast<const uint4*>(lds + row * stride + col);
+  }
+}
+
 }  // namespace
 }  // namespace attn
