@@ -36,11 +36,15 @@ namespace {
 // ------------------------------------------------------------------ forward
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a, int nqt) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdArgs a, int nqt) {
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, STR = D + 8;
-  constexpr int KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * STR];
+  constexpr int KC = D / 16, DB = D / 32, SL = lds_slots(BN, D) * 8;
+  // two named buffers (not one indexed array) so that the compiler can tell
+  // the tile being read from the tile whose direct-to-LDS loads are in flight
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[SL];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[SL];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[SL];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[SL];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
   const int BH = a.B * a.H;
@@ -57,94 +61,95 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a, int nqt) {
   const int myq = wa + (lane & 31);
   const bool qvalid = myq < a.nq;
 
-  bf16x8 qop[KC];
-  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
-
   int lo, hi, wlo = 0, whi = 0;
   mg.key_range(i0, i1, &lo, &hi);
   if (wa < a.nq) mg.key_range(wa, wb, &wlo, &whi);
   const int rlo = qvalid ? mg.row_lo(myq) : 0;
   const int rhi = qvalid ? mg.row_hi(myq) : 0;
   const float sl2 = a.scale * kLog2e;
+  const int t0 = (lo / BN) * BN;
+
+  if (lo < hi) {
+    dma_tile<BN, D, NT>(sK0, K, t0, a.nk, tid);
+    dma_tile<BN, D, NT>(sV0, V, t0, a.nk, tid);
+  }
+  bf16x8 qop[KC];
+  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
 
   float m = -INFINITY, l = 0.f;
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
+  // one key tile [j0, j0 + BN) from LDS: scores, online softmax, O += P V
+  auto tile = [&](const uint16_t* k_l, const uint16_t* v_l, int j0) {
+    if (!(j0 < whi && j0 + BN > wlo)) return;
+    const bool full = mg.tile_full(wa, wb, j0, j0 + BN);
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        s[mb] = mfma32(lds_read8(k_l + (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq),
+                       qop[kc], s[mb]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = s[mb][e] * sl2;
+        if (!full) {
+          const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+          if (key < rlo || key >= rhi) x = -INFINITY;
+        }
+        s[mb][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, xor32(mx));
+    const float mnew = fmaxf(m, mx);
+    const float mu = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = fast_exp2(m - mu);
+    float rs = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(s[mb][e] - mu);
+        s[mb][e] = p;
+        rs += p;
+      }
+    rs += xor32(rs);
+    l = l * alpha + rs;
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+#pragma unroll
+    for (int c = 0; c < BN / 16; ++c) {
+      const bf16x8 pop = acc_chunk(s[c >> 1], c & 1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = mfma32(lds_read_tr8(v_l, STR, 16 * c, 32 * db, lane), pop, oacc[db]);
+    }
+  };
+
   if (lo < hi) {
-    TileLoader<BN, D, NT> kt, vt;
-    const int t0 = (lo / BN) * BN;
-    kt.load(K, t0, a.nk, tid);
-    vt.load(V, t0, a.nk, tid);
-    kt.store(sK[0], STR, tid);
-    vt.store(sV[0], STR, tid);
     __syncthreads();
-    int cur = 0;
-    for (int j0 = t0; j0 < hi; j0 += BN) {
-      const bool has_next = j0 + BN < hi;
-      if (has_next) {
-        kt.load(K, j0 + BN, a.nk, tid);
-        vt.load(V, j0 + BN, a.nk, tid);
+    for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
+      if (j0 + BN < hi) {
+        dma_tile<BN, D, NT>(sK1, K, j0 + BN, a.nk, tid);
+        dma_tile<BN, D, NT>(sV1, V, j0 + BN, a.nk, tid);
       }
-      if (j0 < whi && j0 + BN > wlo) {
-        const bool full = mg.tile_full(wa, wb, j0, j0 + BN);
-        const uint16_t* k_l = sK[cur];
-        const uint16_t* v_l = sV[cur];
-        f32x16 s[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          s[mb] = f32x16{};
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            s[mb] = mfma32(lds_read8(k_l + (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq),
-                           qop[kc], s[mb]);
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float x = s[mb][e] * sl2;
-            if (!full) {
-              const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
-              if (key < rlo || key >= rhi) x = -INFINITY;
-            }
-            s[mb][e] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, xor32(mx));
-        const float mnew = fmaxf(m, mx);
-        const float mu = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = fast_exp2(m - mu);
-        float rs = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float p = fast_exp2(s[mb][e] - mu);
-            s[mb][e] = p;
-            rs += p;
-          }
-        rs += xor32(rs);
-        l = l * alpha + rs;
-        m = mnew;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-#pragma unroll
-        for (int c = 0; c < BN / 16; ++c) {
-          const bf16x8 pop = acc_chunk(s[c >> 1], c & 1);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            oacc[db] = mfma32(lds_read_tr8(v_l, STR, 16 * c, 32 * db, lane), pop, oacc[db]);
-        }
-      }
-      if (has_next) {
-        kt.store(sK[cur ^ 1], STR, tid);
-        vt.store(sV[cur ^ 1], STR, tid);
-      }
+      tile(sK0, sV0, j0);
       __syncthreads();
-      cur ^= 1;
+      if (j0 + BN >= hi) break;
+      if (j0 + 2 * BN < hi) {
+        dma_tile<BN, D, NT>(sK0, K, j0 + 2 * BN, a.nk, tid);
+        dma_tile<BN, D, NT>(sV0, V, j0 + 2 * BN, a.nk, tid);
+      }
+      tile(sK1, sV1, j0 + BN);
+      __syncthreads();
     }
   }
 

@@ -42,6 +42,40 @@ struct TileLoader {
   }
 };
 
+// Direct global -> LDS copy of a ROWS x D bf16 tile whose rows start at r0 of
+// a [n][D] matrix, into the padded LDS layout of row stride D + 8 (gfx950
+// global_load_lds_dwordx4: the 16 bytes each lane loads land at the wave's
+// LDS base + 16 * lane, with no register staging).  The tile is ROWS * SPR
+// 16-byte slots, SPR = D / 8 + 1 per row; slot p is row p / SPR, column chunk
+// p % SPR.  The padding slot of each row receives that row's first chunk and
+// rows >= n receive row n - 1: finite values that every kernel masks out.
+// The LDS array must hold lds_slots(ROWS, D) slots.  Completion is waited for
+// by the caller (s_waitcnt vmcnt(0), which __syncthreads() implies).
+__host__ __device__ constexpr int lds_slots(int rows, int d) {
+  return ((rows * (d / 8 + 1) + 63) / 64) * 64;
+}
+
+template <int ROWS, int D, int NT>
+__device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, int r0, int n,
+                                         int tid) {
+  constexpr int SPR = D / 8 + 1, TOTAL = ROWS * SPR;
+  constexpr int STEPS = (TOTAL + NT - 1) / NT;
+#pragma unroll
+  for (int t = 0; t < STEPS; ++t) {
+    const int wbase = t * NT + (tid & ~63);  // first slot of this wave's 64
+    if (wbase < TOTAL) {
+      const int p = t * NT + tid;
+      const int row = p / SPR, ch = p % SPR;
+      const int gr = min(r0 + row, n - 1);
+      const uint16_t* g = src + (int64_t)gr * D + (ch == SPR - 1 ? 0 : ch * 8);
+      if (p < TOTAL)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)g,
+            (__attribute__((address_space(3))) void*)(lds + wbase * 8), 16, 0, 0);
+    }
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void load_operand_rows(bf16x8 (&op)[D / 16], const uint16_t* rowp,
                                                   bool valid, int gq) {
