@@ -37,14 +37,15 @@ namespace {
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdArgs a, int nqt) {
-  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, STR = D + 8;
-  constexpr int KC = D / 16, DB = D / 32, SL = lds_slots(BN, D) * 8;
+  static_assert(NW == 4, "O staging assumes 4 waves (two 64-row tiles)");
+  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, TE = tile_elems<BN, D>();
+  constexpr int KC = D / 16, DB = D / 32;
   // two named buffers (not one indexed array) so that the compiler can tell
   // the tile being read from the tile whose direct-to-LDS loads are in flight
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[SL];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[SL];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[SL];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[SL];
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
   const int BH = a.B * a.H;
@@ -91,8 +92,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       s[mb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        s[mb] = mfma32(lds_read8(k_l + (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq),
-                       qop[kc], s[mb]);
+        s[mb] = mfma32(lds_row8<D>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const bf16x8 pop = acc_chunk(s[c >> 1], c & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        oacc[db] = mfma32(lds_read_tr8(v_l, STR, 16 * c, 32 * db, lane), pop, oacc[db]);
+        oacc[db] = mfma32(lds_tr8<D>(v_l, 16 * c, 32 * db, lane), pop, oacc[db]);
     }
   };
 
@@ -152,13 +152,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       __syncthreads();
     }
   }
-
-  if (qvalid) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    store_row_bf16<D>((uint16_t*)a.o + ((int64_t)bh * a.nq + myq) * D, oacc, inv, gq);
-    if (gq == 0)
-      a.lse[(int64_t)bh * a.nq + myq] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-  }
+  // every wave is past its last LDS read here (each path above ends in a
+  // barrier, and with no visible key no tile was loaded): O rows go through
+  // sK0 (waves 0, 1) and sV0 (waves 2, 3) for whole-row 16-byte stores
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  acc_to_lds<D>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), oacc, inv, gq);
+  if (qvalid && gq == 0)
+    a.lse[(int64_t)bh * a.nq + myq] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  __syncthreads();
+  uint16_t* O = (uint16_t*)a.o + (int64_t)bh * a.nq * D;
+  store_tile<64, D, NT>(O, i0, a.nq, sK0, tid);
+  store_tile<64, D, NT>(O, i0 + 64, a.nq, sV0, tid);
 }
 
 // ------------------------------------------------------- backward: row sums
@@ -186,13 +190,20 @@ __global__ __launch_bounds__(256) void dsum_bf16_kernel(const uint16_t* __restri
 // ------------------------------------------------------- backward: dK / dV
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void dkdv_bf16_kernel(BwdArgs a, int nkt) {
-  constexpr int NT = NW * 64, BK = 32 * NW, BQ = 32, STR = D + 8;
-  constexpr int KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[2][BQ * STR];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2))) void dkdv_bf16_kernel(BwdArgs a, int nkt) {
+  static_assert(NW == 4, "dK/dV staging assumes 4 waves (two 64-row tiles each)");
+  // query tile: 64 rows, or 32 at D = 128 so that two workgroups fit in LDS
+  constexpr int NT = NW * 64, BK = 32 * NW, BQ = D == 128 ? 32 : 64, TE = tile_elems<BQ, D>();
+  constexpr int KC = D / 16, DB = D / 32, NH = BQ / 32;
+  // Q and dO tiles of BQ query rows, two named buffers each; per buffer the
+  // row statistics: [h*64 .. h*64+31] = lse, [h*64+32 .. h*64+63] = D of
+  // rows 32h .. 32h+31
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG1[TE];
+  __shared__ __attribute__((aligned(16))) float sS0[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float sS1[2 * BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
   const int BH = a.B * a.H;
@@ -212,16 +223,24 @@ __global__ __launch_bounds__(NW * 64) void dkdv_bf16_kernel(BwdArgs a, int nkt) 
   const int myk = wk0 + (lane & 31);
   const bool kvalid = myk < a.nk;
 
-  bf16x8 kop[KC], vop[KC];
-  load_operand_rows<D>(kop, K + (int64_t)myk * D, kvalid, gq);
-  load_operand_rows<D>(vop, V + (int64_t)myk * D, kvalid, gq);
-
   int lo, hi, wlo = 0, whi = 0;
   mg.query_range(k0, k1, &lo, &hi);
   if (wk0 < a.nk) mg.query_range(wk0, wk1, &wlo, &whi);
   const int clo = kvalid ? mg.col_lo(myk) : 0;
   const int chi = kvalid ? mg.col_hi(myk) : 0;
   const float sl2 = a.scale * kLog2e;
+  const int t0 = (lo / BQ) * BQ;
+
+  auto load = [&](uint16_t* q_l, uint16_t* g_l, float* s_l, int r0) {
+    dma_tile<BQ, D, NT>(q_l, Q, r0, a.nq, tid);
+    dma_tile<BQ, D, NT>(g_l, dO, r0, a.nq, tid);
+    if (wave < NH) dma_rows_f32x2(s_l + 64 * wave, LSE, DS, r0 + 32 * wave, a.nq, lane);
+  };
+  if (lo < hi) load(sQ0, sG0, sS0, t0);
+
+  bf16x8 kop[KC], vop[KC];
+  load_operand_rows<D>(kop, K + (int64_t)myk * D, kvalid, gq);
+  load_operand_rows<D>(vop, V + (int64_t)myk * D, kvalid, gq);
 
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -230,98 +249,100 @@ __global__ __launch_bounds__(NW * 64) void dkdv_bf16_kernel(BwdArgs a, int nkt) 
     dvacc[db] = f32x16{};
   }
 
-  if (lo < hi) {
-    TileLoader<BQ, D, NT> qt, ot;
-    float lreg = 0.f, dreg = 0.f;
-    auto load_rowstats = [&](int r0) {
-      if (tid < BQ) {
-        const int r = r0 + tid;
-        const float x = r < a.nq ? LSE[r] : 0.f;
-        lreg = x * kLog2e;
-        dreg = r < a.nq ? DS[r] : 0.f;
+  // one query tile from LDS, in 32-row parts: S, dP, P, dS for this wave's
+  // 32 keys, then dV^T += dO^T P and dK^T += Q^T dS
+  auto tile = [&](const uint16_t* q_l, const uint16_t* g_l, const float* s_l, int i0) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int ih = i0 + 32 * h;
+      if (!(ih < whi && ih + 32 > wlo)) continue;
+      const bool full = mg.tile_full(ih, ih + 32, wk0, wk1) && wk1 == wk0 + 32;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        s = mfma32(lds_row8<D>(q_l, 32 * h, lane & 31, kc, gq), kop[kc], s);
+        dp = mfma32(lds_row8<D>(g_l, 32 * h, lane & 31, kc, gq), vop[kc], dp);
       }
-    };
-    const int t0 = (lo / BQ) * BQ;
-    qt.load(Q, t0, a.nq, tid);
-    ot.load(dO, t0, a.nq, tid);
-    load_rowstats(t0);
-    qt.store(sQ[0], STR, tid);
-    ot.store(sO[0], STR, tid);
-    if (tid < BQ) {
-      sL[0][tid] = lreg;
-      sD[0][tid] = dreg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 L4 = *reinterpret_cast<const f32x4*>(&s_l[64 * h + 8 * i + 4 * gq]);
+        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&s_l[64 * h + 32 + 8 * i + 4 * gq]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * i + j;
+          const int qi = ih + 8 * i + 4 * gq + j;
+          const bool vis = full || (qi >= clo && qi < chi);
+          const float p = vis ? fast_exp2(fmaf(s[e], sl2, -L4[j] * kLog2e)) : 0.f;
+          s[e] = p;
+          dp[e] = p * (dp[e] - D4[j]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pop = acc_chunk(s, c);
+        const bf16x8 dsop = acc_chunk(dp, c);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dvacc[db] = mfma32(lds_tr8<D>(g_l, 32 * h + 16 * c, 32 * db, lane), pop, dvacc[db]);
+          dkacc[db] = mfma32(lds_tr8<D>(q_l, 32 * h + 16 * c, 32 * db, lane), dsop, dkacc[db]);
+        }
+      }
     }
+  };
+
+  if (lo < hi) {
     __syncthreads();
-    int cur = 0;
-    for (int i0 = t0; i0 < hi; i0 += BQ) {
-      const bool has_next = i0 + BQ < hi;
-      if (has_next) {
-        qt.load(Q, i0 + BQ, a.nq, tid);
-        ot.load(dO, i0 + BQ, a.nq, tid);
-        load_rowstats(i0 + BQ);
-      }
-      if (i0 < whi && i0 + BQ > wlo) {
-        const bool full = mg.tile_full(i0, i0 + BQ, wk0, wk1) && wk1 == wk0 + 32;
-        const uint16_t* q_l = sQ[cur];
-        const uint16_t* o_l = sO[cur];
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          s = mfma32(lds_read8(q_l + (lane & 31) * STR + 16 * kc + 8 * gq), kop[kc], s);
-          dp = mfma32(lds_read8(o_l + (lane & 31) * STR + 16 * kc + 8 * gq), vop[kc], dp);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[cur][8 * i + 4 * gq]);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[cur][8 * i + 4 * gq]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = 4 * i + j;
-            const int qi = i0 + 8 * i + 4 * gq + j;
-            const bool vis = full || (qi >= clo && qi < chi);
-            const float p = vis ? fast_exp2(s[e] * sl2 - L4[j]) : 0.f;
-            s[e] = p;
-            dp[e] = p * (dp[e] - D4[j]);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < BQ / 16; ++c) {
-          const bf16x8 pop = acc_chunk(s, c);
-          const bf16x8 dsop = acc_chunk(dp, c);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dvacc[db] = mfma32(lds_read_tr8(o_l, STR, 16 * c, 32 * db, lane), pop, dvacc[db]);
-            dkacc[db] = mfma32(lds_read_tr8(q_l, STR, 16 * c, 32 * db, lane), dsop, dkacc[db]);
-          }
-        }
-      }
-      if (has_next) {
-        qt.store(sQ[cur ^ 1], STR, tid);
-        ot.store(sO[cur ^ 1], STR, tid);
-        if (tid < BQ) {
-          sL[cur ^ 1][tid] = lreg;
-          sD[cur ^ 1][tid] = dreg;
-        }
-      }
+    for (int i0 = t0; i0 < hi; i0 += 2 * BQ) {
+      if (i0 + BQ < hi) load(sQ1, sG1, sS1, i0 + BQ);
+      tile(sQ0, sG0, sS0, i0);
       __syncthreads();
-      cur ^= 1;
+      if (i0 + BQ >= hi) break;
+      if (i0 + 2 * BQ < hi) load(sQ0, sG0, sS0, i0 + 2 * BQ);
+      tile(sQ1, sG1, sS1, i0 + BQ);
+      __syncthreads();
     }
   }
-
-  if (kvalid) {
-    store_row_bf16<D>((uint16_t*)a.dk + ((int64_t)bh * a.nk + myk) * D, dkacc, a.scale, gq);
-    store_row_bf16<D>((uint16_t*)a.dv + ((int64_t)bh * a.nk + myk) * D, dvacc, 1.f, gq);
+  // dK and dV rows go through the four tile buffers for whole-row stores
+  uint16_t* dK = (uint16_t*)a.dk + (int64_t)bh * a.nk * D;
+  uint16_t* dV = (uint16_t*)a.dv + (int64_t)bh * a.nk * D;
+  if constexpr (BQ == 64) {
+    // 64-row buffers: dK through sQ0 / sG0, dV through sQ1 / sG1
+    const int row = 32 * (wave & 1) + (lane & 31);
+    acc_to_lds<D>(wave < 2 ? sQ0 : sG0, row, dkacc, a.scale, gq);
+    acc_to_lds<D>(wave < 2 ? sQ1 : sG1, row, dvacc, 1.f, gq);
+    __syncthreads();
+    store_tile<64, D, NT>(dK, k0, a.nk, sQ0, tid);
+    store_tile<64, D, NT>(dK, k0 + 64, a.nk, sG0, tid);
+    store_tile<64, D, NT>(dV, k0, a.nk, sQ1, tid);
+    store_tile<64, D, NT>(dV, k0 + 64, a.nk, sG1, tid);
+  } else {
+    // 32-row buffers, one per wave: dK first, then dV
+    uint16_t* mine = wave == 0 ? sQ0 : wave == 1 ? sG0 : wave == 2 ? sQ1 : sG1;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass) __syncthreads();
+      acc_to_lds<D>(mine, lane & 31, pass ? dvacc : dkacc, pass ? 1.f : a.scale, gq);
+      __syncthreads();
+      uint16_t* dst = pass ? dV : dK;
+      store_tile<32, D, NT>(dst, k0, a.nk, sQ0, tid);
+      store_tile<32, D, NT>(dst, k0 + 32, a.nk, sG0, tid);
+      store_tile<32, D, NT>(dst, k0 + 64, a.nk, sQ1, tid);
+      store_tile<32, D, NT>(dst, k0 + 96, a.nk, sG1, tid);
+    }
   }
 }
 
 // ------------------------------------------------------------ backward: dQ
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void dq_bf16_kernel(BwdArgs a, int nqt) {
-  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, STR = D + 8;
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void dq_bf16_kernel(BwdArgs a, int nqt) {
+  static_assert(NW == 4, "dQ staging assumes 4 waves (two 64-row tiles)");
+  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, TE = tile_elems<BN, D>();
   constexpr int KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * STR];
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
   const int BH = a.B * a.H;
@@ -339,86 +360,85 @@ __global__ __launch_bounds__(NW * 64) void dq_bf16_kernel(BwdArgs a, int nqt) {
   const int myq = wa + (lane & 31);
   const bool qvalid = myq < a.nq;
 
-  bf16x8 qop[KC], dop[KC];
-  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
-  load_operand_rows<D>(dop, dO + (int64_t)myq * D, qvalid, gq);
-  const float lse2 = qvalid ? a.lse[(int64_t)bh * a.nq + myq] * kLog2e : 0.f;
-  const float dsv = qvalid ? a.dsum[(int64_t)bh * a.nq + myq] : 0.f;
-
   int lo, hi, wlo = 0, whi = 0;
   mg.key_range(i0, i1, &lo, &hi);
   if (wa < a.nq) mg.key_range(wa, wb, &wlo, &whi);
   const int rlo = qvalid ? mg.row_lo(myq) : 0;
   const int rhi = qvalid ? mg.row_hi(myq) : 0;
   const float sl2 = a.scale * kLog2e;
+  const int t0 = (lo / BN) * BN;
+
+  if (lo < hi) {
+    dma_tile<BN, D, NT>(sK0, K, t0, a.nk, tid);
+    dma_tile<BN, D, NT>(sV0, V, t0, a.nk, tid);
+  }
+  bf16x8 qop[KC], dop[KC];
+  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
+  load_operand_rows<D>(dop, dO + (int64_t)myq * D, qvalid, gq);
+  const float lse2 = qvalid ? a.lse[(int64_t)bh * a.nq + myq] * kLog2e : 0.f;
+  const float dsv = qvalid ? a.dsum[(int64_t)bh * a.nq + myq] : 0.f;
 
   f32x16 dqacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
+  // one key tile [j0, j0 + BN): S^T, dP^T, dS^T per 32-key half (packed to
+  // bf16 right away to keep the live set small), then dQ^T += K^T dS^T
+  auto tile = [&](const uint16_t* k_l, const uint16_t* v_l, int j0) {
+    if (!(j0 < whi && j0 + BN > wlo)) return;
+    const bool full = mg.tile_full(wa, wb, j0, j0 + BN);
+    bf16x8 dsop[BN / 16];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        s = mfma32(lds_row8<D>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], s);
+        dp = mfma32(lds_row8<D>(v_l, mb * 32, lane & 31, kc, gq), dop[kc], dp);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        bool vis = true;
+        if (!full) {
+          const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+          vis = key >= rlo && key < rhi;
+        }
+        const float p = vis ? fast_exp2(s[e] * sl2 - lse2) : 0.f;
+        s[e] = p * (dp[e] - dsv);
+      }
+      dsop[2 * mb] = acc_chunk(s, 0);
+      dsop[2 * mb + 1] = acc_chunk(s, 1);
+    }
+#pragma unroll
+    for (int c = 0; c < BN / 16; ++c)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqacc[db] = mfma32(lds_tr8<D>(k_l, 16 * c, 32 * db, lane), dsop[c], dqacc[db]);
+  };
+
   if (lo < hi) {
-    TileLoader<BN, D, NT> kt, vt;
-    const int t0 = (lo / BN) * BN;
-    kt.load(K, t0, a.nk, tid);
-    vt.load(V, t0, a.nk, tid);
-    kt.store(sK[0], STR, tid);
-    vt.store(sV[0], STR, tid);
     __syncthreads();
-    int cur = 0;
-    for (int j0 = t0; j0 < hi; j0 += BN) {
-      const bool has_next = j0 + BN < hi;
-      if (has_next) {
-        kt.load(K, j0 + BN, a.nk, tid);
-        vt.load(V, j0 + BN, a.nk, tid);
+    for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
+      if (j0 + BN < hi) {
+        dma_tile<BN, D, NT>(sK1, K, j0 + BN, a.nk, tid);
+        dma_tile<BN, D, NT>(sV1, V, j0 + BN, a.nk, tid);
       }
-      if (j0 < whi && j0 + BN > wlo) {
-        const bool full = mg.tile_full(wa, wb, j0, j0 + BN);
-        const uint16_t* k_l = sK[cur];
-        const uint16_t* v_l = sV[cur];
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          s[mb] = f32x16{};
-          dp[mb] = f32x16{};
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            s[mb] = mfma32(lds_read8(k_l + (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq),
-                           qop[kc], s[mb]);
-            dp[mb] = mfma32(lds_read8(v_l + (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq),
-                            dop[kc], dp[mb]);
-          }
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            bool vis = true;
-            if (!full) {
-              const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
-              vis = key >= rlo && key < rhi;
-            }
-            const float p = vis ? fast_exp2(s[mb][e] * sl2 - lse2) : 0.f;
-            s[mb][e] = p * (dp[mb][e] - dsv);
-          }
-#pragma unroll
-        for (int c = 0; c < BN / 16; ++c) {
-          const bf16x8 dsop = acc_chunk(s[c >> 1], c & 1);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            dqacc[db] = mfma32(lds_read_tr8(k_l, STR, 16 * c, 32 * db, lane), dsop, dqacc[db]);
-        }
-      }
-      if (has_next) {
-        kt.store(sK[cur ^ 1], STR, tid);
-        vt.store(sV[cur ^ 1], STR, tid);
-      }
+      tile(sK0, sV0, j0);
       __syncthreads();
-      cur ^= 1;
+      if (j0 + BN >= hi) break;
+      if (j0 + 2 * BN < hi) {
+        dma_tile<BN, D, NT>(sK0, K, j0 + 2 * BN, a.nk, tid);
+        dma_tile<BN, D, NT>(sV0, V, j0 + 2 * BN, a.nk, tid);
+      }
+      tile(sK1, sV1, j0 + BN);
+      __syncthreads();
     }
   }
-
-  if (qvalid)
-    store_row_bf16<D>((uint16_t*)a.dq + ((int64_t)bh * a.nq + myq) * D, dqacc, a.scale, gq);
+  acc_to_lds<D>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), dqacc, a.scale, gq);
+  __syncthreads();
+  uint16_t* dQ = (uint16_t*)a.dq + (int64_t)bh * a.nq * D;
+  store_tile<64, D, NT>(dQ, i0, a.nq, sK0, tid);
+  store_tile<64, D, NT>(dQ, i0 + 64, a.nq, sV0, tid);
 }
 
 template <int D>

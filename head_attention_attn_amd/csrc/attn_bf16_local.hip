@@ -42,9 +42,9 @@ __device__ __forceinline__ bool local_vis(int qi, int kj, int n, int wshift) {
 
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int wshift) {
-  constexpr int NT = 128, STR = D + 8, KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kTile * STR];
+  constexpr int NT = 128, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[TE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
   const int bh = blockIdx.x / ntile;
@@ -55,15 +55,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void f
   const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * n * D;
   const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * n * D;
 
-  TileLoader<kTile, D, NT> kt, vt;
-  kt.load(K, t0, n, tid);
-  vt.load(V, t0, n, tid);
+  dma_tile<kTile, D, NT>(sK, K, t0, n, tid);
+  dma_tile<kTile, D, NT>(sV, V, t0, n, tid);
   const int myq = t0 + wave * 32 + (lane & 31);
   const bool qvalid = myq < n;
   bf16x8 qop[KC];
   load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
-  kt.store(sK, STR, tid);
-  vt.store(sV, STR, tid);
   __syncthreads();
 
   f32x16 s[2];
@@ -72,8 +69,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void f
     s[mb] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      s[mb] = mfma32(lds_read8(sK + (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq), qop[kc],
-                     s[mb]);
+      s[mb] = mfma32(lds_row8<D>(sK, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
   }
   const bool full = wshift == 6 && t0 + kTile <= n;
   const float sl2 = a.scale * kLog2e;
@@ -111,26 +107,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void f
     const bf16x8 pop = acc_chunk(s[c >> 1], c & 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      oacc[db] = mfma32(lds_read_tr8(sV, STR, 16 * c, 32 * db, lane), pop, oacc[db]);
+      oacc[db] = mfma32(lds_tr8<D>(sV, 16 * c, 32 * db, lane), pop, oacc[db]);
   }
   // O rows through LDS (sK is free once every wave is past its products) so
   // that the global stores are whole rows, 16 bytes per lane
   __syncthreads();
-  acc_to_lds<D>(sK, STR, wave * 32 + (lane & 31), oacc, qvalid ? 1.f / l : 0.f, gq);
+  acc_to_lds<D>(sK, wave * 32 + (lane & 31), oacc, qvalid ? 1.f / l : 0.f, gq);
   if (qvalid && gq == 0) a.lse[(int64_t)bh * n + myq] = (mb2 + log2f(l)) * kLn2;
   __syncthreads();
-  store_tile<kTile, D, NT>((uint16_t*)a.o + (int64_t)bh * n * D, t0, n, sK, STR, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.o + (int64_t)bh * n * D, t0, n, sK, tid);
 }
 
 // ----------------------------------------------------------------- backward
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, int wshift) {
-  constexpr int NT = 256, STR = D + 8, KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kTile * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kTile * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[kTile * STR];  // dO
+  constexpr int NT = 256, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[TE];  // dO
   __shared__ __attribute__((aligned(16))) float sL[kTile];           // lse * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[kTile];           // D_i
 
@@ -140,20 +136,13 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
   const int n = a.nq;
   const int64_t base = (int64_t)bh * n * D;
 
-  {
-    TileLoader<kTile, D, NT> lq, lk, lv, lg;
-    lq.load((const uint16_t*)a.q + base, t0, n, tid);
-    lk.load((const uint16_t*)a.k + base, t0, n, tid);
-    lv.load((const uint16_t*)a.v + base, t0, n, tid);
-    lg.load((const uint16_t*)a.dout + base, t0, n, tid);
-    if (tid < kTile) {
-      const int r = t0 + tid;
-      sL[tid] = r < n ? a.lse[(int64_t)bh * n + r] * kLog2e : 0.f;
-    }
-    lq.store(sQ, STR, tid);
-    lk.store(sK, STR, tid);
-    lv.store(sV, STR, tid);
-    lg.store(sG, STR, tid);
+  dma_tile<kTile, D, NT>(sQ, (const uint16_t*)a.q + base, t0, n, tid);
+  dma_tile<kTile, D, NT>(sK, (const uint16_t*)a.k + base, t0, n, tid);
+  dma_tile<kTile, D, NT>(sV, (const uint16_t*)a.v + base, t0, n, tid);
+  dma_tile<kTile, D, NT>(sG, (const uint16_t*)a.dout + base, t0, n, tid);
+  if (tid < kTile) {
+    const int r = t0 + tid;
+    sL[tid] = r < n ? a.lse[(int64_t)bh * n + r] * kLog2e : 0.f;
   }
   __syncthreads();
 
@@ -181,10 +170,10 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
       y[mb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const int kr = (mb * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq;
-        const int qr = own * STR + 16 * kc + 8 * gq;
-        x[mb] = mfma32(lds_read8(sK + kr), lds_read8(sQ + qr), x[mb]);
-        y[mb] = mfma32(lds_read8(sV + kr), lds_read8(sG + qr), y[mb]);
+        x[mb] = mfma32(lds_row8<D>(sK, 32 * mb, lane & 31, kc, gq), lds_row8<D>(sQ, 0, own, kc, gq),
+                       x[mb]);
+        y[mb] = mfma32(lds_row8<D>(sV, 32 * mb, lane & 31, kc, gq), lds_row8<D>(sG, 0, own, kc, gq),
+                       y[mb]);
       }
     }
     float dsum = 0.f;
@@ -212,10 +201,10 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
       y[qt] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const int qr = (qt * 32 + (lane & 31)) * STR + 16 * kc + 8 * gq;
-        const int kr = own * STR + 16 * kc + 8 * gq;
-        x[qt] = mfma32(lds_read8(sQ + qr), lds_read8(sK + kr), x[qt]);
-        y[qt] = mfma32(lds_read8(sG + qr), lds_read8(sV + kr), y[qt]);
+        x[qt] = mfma32(lds_row8<D>(sQ, 32 * qt, lane & 31, kc, gq), lds_row8<D>(sK, 0, own, kc, gq),
+                       x[qt]);
+        y[qt] = mfma32(lds_row8<D>(sG, 32 * qt, lane & 31, kc, gq), lds_row8<D>(sV, 0, own, kc, gq),
+                       y[qt]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -234,7 +223,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
         const bf16x8 pop = acc_chunk(x[qt], c);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc1[db] = mfma32(lds_read_tr8(sG, STR, 32 * qt + 16 * c, 32 * db, lane), pop, acc1[db]);
+          acc1[db] = mfma32(lds_tr8<D>(sG, 32 * qt + 16 * c, 32 * db, lane), pop, acc1[db]);
       }
     }
   }
@@ -248,7 +237,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
       const bf16x8 dsop = acc_chunk(x[c >> 1], c & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        acc0[db] = mfma32(lds_read_tr8(sK, STR, 16 * c, 32 * db, lane), dsop, acc0[db]);
+        acc0[db] = mfma32(lds_tr8<D>(sK, 16 * c, 32 * db, lane), dsop, acc0[db]);
     }
   } else {
 #pragma unroll
@@ -264,21 +253,21 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
         const bf16x8 dsop = acc_chunk(x[qt], c);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc0[db] = mfma32(lds_read_tr8(sQ, STR, 32 * qt + 16 * c, 32 * db, lane), dsop, acc0[db]);
+          acc0[db] = mfma32(lds_tr8<D>(sQ, 32 * qt + 16 * c, 32 * db, lane), dsop, acc0[db]);
       }
     }
   }
   __syncthreads();
   if (dq_wave) {
-    acc_to_lds<D>(sQ, STR, own, acc0, a.scale, gq);
+    acc_to_lds<D>(sQ, own, acc0, a.scale, gq);
   } else {
-    acc_to_lds<D>(sK, STR, own, acc0, a.scale, gq);
-    acc_to_lds<D>(sV, STR, own, acc1, 1.f, gq);
+    acc_to_lds<D>(sK, own, acc0, a.scale, gq);
+    acc_to_lds<D>(sV, own, acc1, 1.f, gq);
   }
   __syncthreads();
-  store_tile<kTile, D, NT>((uint16_t*)a.dq + base, t0, n, sQ, STR, tid);
-  store_tile<kTile, D, NT>((uint16_t*)a.dk + base, t0, n, sK, STR, tid);
-  store_tile<kTile, D, NT>((uint16_t*)a.dv + base, t0, n, sV, STR, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.dq + base, t0, n, sQ, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.dk + base, t0, n, sK, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.dv + base, t0, n, sV, tid);
 }
 
 int shift_of(int w) {

@@ -1,6 +1,26 @@
-// bf16_tile.hpp -- tile staging and operand helpers shared by the bf16
-// attention kernels (global -> register -> LDS tile copies, MFMA operand
-// loads of whole rows, bf16 row stores of transposed accumulators).
+// bf16_tile.hpp -- LDS tile layout and tile movement shared by the bf16
+// attention kernels: direct global -> LDS tile loads, MFMA operand reads
+// (row-wise and transposed), accumulator -> LDS staging and LDS -> global
+// row stores.
+//
+// LDS tile layout.  A ROWS x D bf16 tile is stored row-major with row stride
+// tstride<D>() elements; within row r the 16-byte chunk c (elements 8c ..
+// 8c+7) sits at chunk position c ^ ((r / 4) % 4).  gfx950's LDS has 64
+// four-byte banks and serves a ds_read_b128 16 lanes at a time and a
+// ds_read_b64 / ds_read_b64_tr_b16 32 lanes at a time (measured with
+// SQ_LDS_BANK_CONFLICT on MI355X).  The kernels read tiles in two patterns:
+//   row reads   lanes 0..15 read the same chunk of 16 consecutive rows;
+//   transposed  lanes 0..31 read 4 consecutive rows (a multiple of 4 first)
+//               x 4 consecutive chunks (a multiple of 4 first).
+// With a stride of 16 or 48 banks (mod 64) -- 160 elements for D = 128, 96 for
+// D = 96 and D = 64 -- rows r .. r+3 start in four different 16-bank groups,
+// which serves the transposed pattern; the row pattern's 16 rows then fall
+// four to a group, and the XOR of the low two chunk bits with (r / 4) % 4
+// spreads those four over the group's four 16-byte slots.  Both patterns run
+// in one pass per 16 / 32 lanes.  The XOR touches only the low two chunk bits
+// and depends on row bits 2-3 only, so most loop-varying offsets stay
+// compile-time constants (ds_read immediate offsets) rather than per-lane
+// address registers.
 #pragma once
 
 #include "attn_common.hpp"
@@ -12,70 +32,110 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Cooperative global -> register -> LDS staging of a ROWS x D bf16 tile whose
-// rows start at r0 of a [n][D] matrix; rows >= n read as zero.
-template <int ROWS, int D, int NT>
-struct TileLoader {
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int TOTAL = ROWS * CPR;
-  static constexpr int CH = (TOTAL + NT - 1) / NT;    // chunks per thread
-  uint4 r[CH];
-
-  __device__ __forceinline__ void load(const uint16_t* src, int r0, int n, int tid) {
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int gr = r0 + row;
-      r[t] = (c < TOTAL && gr < n)
-                 ? *reinterpret_cast<const uint4*>(src + (int64_t)gr * D + col)
-                 : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int stride, int tid) const {
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int c = tid + t * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      if (c < TOTAL) *reinterpret_cast<uint4*>(lds + row * stride + col) = r[t];
-    }
-  }
-};
-
-// Direct global -> LDS copy of a ROWS x D bf16 tile whose rows start at r0 of
-// a [n][D] matrix, into the padded LDS layout of row stride D + 8 (gfx950
-// global_load_lds_dwordx4: the 16 bytes each lane loads land at the wave's
-// LDS base + 16 * lane, with no register staging).  The tile is ROWS * SPR
-// 16-byte slots, SPR = D / 8 + 1 per row; slot p is row p / SPR, column chunk
-// p % SPR.  The padding slot of each row receives that row's first chunk and
-// rows >= n receive row n - 1: finite values that every kernel masks out.
-// The LDS array must hold lds_slots(ROWS, D) slots.  Completion is waited for
-// by the caller (s_waitcnt vmcnt(0), which __syncthreads() implies).
-__host__ __device__ constexpr int lds_slots(int rows, int d) {
-  return ((rows * (d / 8 + 1) + 63) / 64) * 64;
+template <int D>
+__host__ __device__ constexpr int tstride() {
+  static_assert(D == 64 || D == 96 || D == 128, "head dim");
+  return D == 128 ? 160 : 96;
 }
 
+// element offset of (row r, column col) in a tile; col % 4 == 0
+template <int D>
+__device__ __forceinline__ int toff(int r, int col) {
+  return r * tstride<D>() + ((((col >> 3) ^ ((r >> 2) & 3)) << 3) | (col & 7));
+}
+
+// The same offset for row r0 + rl, column c0 + cl, written so that the part
+// from r0 (a multiple of 16) and c0 (a multiple of 32) -- compile-time values
+// in the kernels' unrolled loops -- is a plain sum: the swizzle then depends
+// on the per-lane rl, cl only, and the compiler folds r0, c0 into the
+// instruction's immediate offset.  0 <= cl < 32.
+template <int D>
+__device__ __forceinline__ int toff2(int r0, int rl, int c0, int cl) {
+  return (r0 + rl) * tstride<D>() + c0 + (((((cl >> 3) & 3) ^ ((rl >> 2) & 3)) << 3) | (cl & 7));
+}
+
+// elements of a ROWS-row tile
+template <int ROWS, int D>
+__host__ __device__ constexpr int tile_elems() {
+  return ROWS * tstride<D>();
+}
+
+// MFMA operand from a row read: 8 consecutive bf16 of row r0 + rl at columns
+// 16 kc + 8 gq .. +7 (the contraction runs along the row); r0 % 16 == 0.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* tile, int r0, int rl, int kc, int gq) {
+  return *reinterpret_cast<const bf16x8*>(
+      tile + toff2<D>(r0, rl, 32 * (kc >> 1), 16 * (kc & 1) + 8 * gq));
+}
+
+// Transposed operand read (ds_read_b64_tr_b16, see mfma.hpp): the 8
+// contraction elements of an MFMA operand whose free index is the tile column
+// c0 + lane % 32 and whose contraction runs over tile rows; slots 0..3 are
+// rows r0 + 4g + e, slots 4..7 rows r0 + 8 + 4g + e (g = lane / 32,
+// e = 0..3) -- the row order of a 32x32 accumulator's 16-row chunk, so it
+// pairs with acc_chunk().  r0 % 16 == 0, c0 % 32 == 0.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr8(const uint16_t* tile, int r0, int c0, int lane) {
+  const int grp = lane >> 4, li = lane & 15;
+  const int e = li >> 2, r = li & 3;
+  const int g = grp >> 1, half = grp & 1;
+  const int rl = 4 * g + e, cl = 16 * half + 4 * r;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + toff2<D>(r0, rl, c0, cl)));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(tile + toff2<D>(r0, rl + 8, c0, cl)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Direct global -> LDS load of a ROWS x D bf16 tile (rows r0 .. r0+ROWS-1 of a
+// [n][D] matrix) into the tile layout, by NT threads.  gfx950's
+// global_load_lds_dwordx4 puts the 16 bytes each lane loads at the wave's LDS
+// base + 16 * lane, with no register staging: lane slot p is LDS chunk
+// position p, so the lane fetches the logical chunk that the layout stores
+// there; lanes on padding slots are switched off.  Rows >= n are filled from
+// row n - 1 (finite values that every kernel masks out).  The loads count on
+// vmcnt; the caller waits for them (__syncthreads() does) before reading.
 template <int ROWS, int D, int NT>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, int r0, int n,
                                          int tid) {
-  constexpr int SPR = D / 8 + 1, TOTAL = ROWS * SPR;
+  constexpr int CPR = D / 8, SPR = tstride<D>() / 8, TOTAL = ROWS * SPR;
+  static_assert(TOTAL % 64 == 0, "whole waves per tile");
   constexpr int STEPS = (TOTAL + NT - 1) / NT;
+  // uniform base plus a 32-bit per-lane offset (the scalar-base addressing
+  // form of the load: one address VGPR per load instead of two)
+  const uint16_t* base = src + (int64_t)r0 * D;
+  const int last = n - 1 - r0;
 #pragma unroll
   for (int t = 0; t < STEPS; ++t) {
     const int wbase = t * NT + (tid & ~63);  // first slot of this wave's 64
     if (wbase < TOTAL) {
-      const int p = t * NT + tid;
-      const int row = p / SPR, ch = p % SPR;
-      const int gr = min(r0 + row, n - 1);
-      const uint16_t* g = src + (int64_t)gr * D + (ch == SPR - 1 ? 0 : ch * 8);
-      if (p < TOTAL)
+      const int p = wbase + (tid & 63);
+      const int row = p / SPR, phys = p % SPR;
+      if (phys < CPR) {
+        const int ch = phys ^ ((row >> 2) & 3);
+        const uint32_t off = (uint32_t)(min(row, last) * (2 * D) + ch * 16);  // bytes
         __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)g,
+            (const __attribute__((address_space(1))) void*)((const char*)base + off),
             (__attribute__((address_space(3))) void*)(lds + wbase * 8), 16, 0, 0);
+      }
     }
   }
 }
 
+// Direct global -> LDS load of 64 fp32 values by one wave: lanes 0..31 take
+// a[r0 + lane], lanes 32..63 take b[r0 + lane - 32] (indices clamped to
+// n - 1), landing at lds[lane].
+__device__ __forceinline__ void dma_rows_f32x2(float* lds, const float* a, const float* b, int r0,
+                                               int n, int lane) {
+  const int r = min(r0 + (lane & 31), n - 1);
+  const float* g = (lane < 32 ? a : b) + r;
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// Global -> register MFMA operand of one row (lane l: row l % 32, chunks
+// 2kc + l / 32); rows that are not valid read as zero.
 template <int D>
 __device__ __forceinline__ void load_operand_rows(bf16x8 (&op)[D / 16], const uint16_t* rowp,
                                                   bool valid, int gq) {
@@ -90,45 +150,30 @@ __device__ __forceinline__ void load_operand_rows(bf16x8 (&op)[D / 16], const ui
   }
 }
 
-// Store a transposed 32-column accumulator block set (columns = this lane's
-// row of the output, rows = d) as bf16: d = 32*db + 8*i + 4*gq + j.
+// Write a transposed accumulator set (accumulator rows = the d columns, this
+// lane's accumulator column = tile row `row`) into an LDS tile as
+// bf16, scaled by `mul`: element (row, 32*db + 8*i + 4*gq + j).  Output rows
+// go through LDS so that store_tile() writes them with coalesced 16-byte
+// stores (storing one row per lane would scatter 8-byte pieces over 32 rows
+// per instruction).
 template <int D>
-__device__ __forceinline__ void store_row_bf16(uint16_t* rowp, const f32x16 (&acc)[D / 32],
-                                               float mul, int gq) {
+__device__ __forceinline__ void acc_to_lds(uint16_t* tile, int row, const f32x16 (&acc)[D / 32],
+                                           float mul, int gq) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint2*>(rowp + 32 * db + 8 * i + 4 * gq) =
+      *reinterpret_cast<uint2*>(tile + toff2<D>(0, row, 32 * db, 8 * i + 4 * gq)) =
           pack_bf16x4(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul,
                       acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
 }
 
-// Write a transposed accumulator set (rows = d, this lane's column = output
-// row `row` of an LDS tile) into the LDS tile as bf16, scaled by `mul`:
-// element (row, 32*db + 8*i + 4*gq + j).  Used to turn per-lane output rows
-// into a row-major tile that TileStorer writes out with coalesced 16-byte
-// stores (a direct store of one row per lane would scatter 8-byte pieces over
-// 32 rows per instruction).
-template <int D>
-__device__ __forceinline__ void acc_to_lds(uint16_t* tile, int stride, int row,
-                                           const f32x16 (&acc)[D / 32], float mul, int gq) {
-  uint16_t* rp = tile + row * stride;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint2*>(rp + 32 * db + 8 * i + 4 * gq) =
-          pack_bf16x4(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul,
-                      acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
-}
-
-// Cooperative LDS -> global copy of a ROWS x D bf16 tile to rows r0.. of a
-// [n][D] matrix, 16 bytes per lane per step, consecutive lanes on
-// consecutive addresses; rows >= n are not written.
+// LDS -> global copy of a ROWS x D tile to rows r0 .. of a [n][D]
+// matrix by NT threads, 16 bytes per lane per step on consecutive addresses;
+// rows >= n are not written.
 template <int ROWS, int D, int NT>
 __device__ __forceinline__ void store_tile(uint16_t* dst, int r0, int n, const uint16_t* lds,
-                                           int stride, int tid) {
+                                           int tid) {
   constexpr int CPR = D / 8, TOTAL = ROWS * CPR, CH = (TOTAL + NT - 1) / NT;
 #pragma unroll
   for (int t = 0; t < CH; ++t) {
@@ -136,7 +181,7 @@ __device__ __forceinline__ void store_tile(uint16_t* dst, int r0, int n, const u
     const int row = c / CPR, col = (c % CPR) * 8;
     if (c < TOTAL && r0 + row < n)
       *reinterpret_cast<uint4*>(dst + (int64_t)(r0 + row) * D + col) =
-          *reinterpret_cast<const uint4*>(lds + row * stride + col);
+          *reinterpret_cast<const uint4*>(lds + toff<D>(row, col));
   }
 }
 

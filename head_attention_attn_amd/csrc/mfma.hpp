@@ -34,37 +34,8 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16-byte LDS read of 8 consecutive bf16 (ds_read_b128)
-__device__ __forceinline__ bf16x8 lds_read8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// Transposed operand read.  `tile` is a row-major bf16 tile in LDS with row
-// stride `stride` elements.  Returns, for this lane, the 8 contraction
-// elements of an MFMA A/B operand whose free index is the tile column
-// c0 + (lane % 32) and whose contraction runs over tile rows: slots 0..3 are
-// rows r0 + 4*g + e, slots 4..7 are rows r0 + 8 + 4*g + e (g = lane / 32,
-// e = 0..3).  This row order is exactly the row order in which a 32x32
-// accumulator stores a 16-row chunk (rows 8*i + 4*g + j, i = 2c, 2c + 1), so
-// it pairs with acc_chunk() below.
-__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* tile, int stride, int r0, int c0,
-                                               int lane) {
-  const int grp = lane >> 4;        // 16-lane group 0..3
-  const int li = lane & 15;
-  const int e = li >> 2, r = li & 3;
-  const int g = grp >> 1;           // contraction-slot group
-  const int half = grp & 1;         // which 16 of the 32 columns
-  const uint16_t* p0 = tile + (r0 + 4 * g + e) * stride + c0 + 16 * half + 4 * r;
-  const uint16_t* p1 = p0 + 8 * stride;
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
 // Accumulator entries 8c .. 8c+7 of a 32x32 tile, rounded to bf16: the rows
-// (8*(2c) + 4g + j, 8*(2c+1) + 4g + j) of chunk c in the order lds_read_tr8
+// (8*(2c) + 4g + j, 8*(2c+1) + 4g + j) of chunk c in the order the transposed LDS read
 // uses, ready to be the other operand of a contraction over those rows.
 __device__ __forceinline__ bf16x8 acc_chunk(const f32x16& acc, int c) {
   f32x8 v;
