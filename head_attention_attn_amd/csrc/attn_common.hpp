@@ -33,6 +33,8 @@
 namespace attn {
 
 enum MaskMode : int { kNone = 0, kCausal = 1, kSliding = 2, kBlock = 3 };
+// kernel template argument: the mask mode is read from MaskGeom at run time
+constexpr int kAnyMask = -1;
 
 struct MaskGeom {
   int mode;

@@ -123,6 +123,36 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, int
   }
 }
 
+// Register-staged tile load: global -> registers now, registers -> LDS (in
+// the tile layout) later.  Unlike the direct-to-LDS load, a barrier between
+// the two does not wait for the global loads (a barrier waits for LDS
+// traffic only), so a tile can be fetched a whole pipeline step before it is
+// written.  Rows >= n read as row n - 1 (finite values the kernels mask).
+template <int ROWS, int D, int NT>
+struct RegTile {
+  static constexpr int CPR = D / 8, TOTAL = ROWS * CPR, CH = (TOTAL + NT - 1) / NT;
+  uint4 r[CH];
+
+  __device__ __forceinline__ void load(const uint16_t* src, int r0, int n, int tid) {
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const int c = tid + t * NT;
+      if (TOTAL % NT == 0 || c < TOTAL) {
+        const int row = min(r0 + c / CPR, n - 1);
+        r[t] = *reinterpret_cast<const uint4*>(src + (int64_t)row * D + (c % CPR) * 8);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const int c = tid + t * NT;
+      if (TOTAL % NT == 0 || c < TOTAL)
+        *reinterpret_cast<uint4*>(lds + toff<D>(c / CPR, (c % CPR) * 8)) = r[t];
+    }
+  }
+};
+
 // Direct global -> LDS load of 64 fp32 values by one wave: lanes 0..31 take
 // a[r0 + lane], lanes 32..63 take b[r0 + lane - 32] (indices clamped to
 // n - 1), landing at lds[lane].
