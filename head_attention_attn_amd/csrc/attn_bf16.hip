@@ -47,7 +47,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
+  const int wave = wave_id(tid);
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // longest causal rows first
@@ -219,7 +220,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   __shared__ __attribute__((aligned(16))) float sS0[2 * BQ];
   __shared__ __attribute__((aligned(16))) float sS1[2 * BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
+  const int wave = wave_id(tid);
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int kt = (int)(blockIdx.x / BH);  // causal: low key tiles see the most queries
@@ -403,7 +405,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   __shared__ __attribute__((aligned(16))) uint16_t sP2[PE];
   __shared__ __attribute__((aligned(16))) uint16_t sD2[PE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
+  const int wave = wave_id(tid);
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int kt = (int)(blockIdx.x / BH);  // causal: low key tiles see the most queries
@@ -600,7 +603,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
+  const int wave = wave_id(tid);
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);

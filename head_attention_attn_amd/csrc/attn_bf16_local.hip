@@ -46,7 +46,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void f
   __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[TE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
+  const int wave = wave_id(tid);
   const int bh = blockIdx.x / ntile;
   const int t0 = (blockIdx.x % ntile) * kTile;
   const int n = a.nq;
@@ -130,7 +131,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
   __shared__ __attribute__((aligned(16))) float sL[kTile];           // lse * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[kTile];           // D_i
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
+  const int wave = wave_id(tid);
   const int bh = blockIdx.x / ntile;
   const int t0 = (blockIdx.x % ntile) * kTile;
   const int n = a.nq;

@@ -54,4 +54,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// Wave index within the workgroup, marked wave-uniform: everything derived
+// from it (the wave's rows or keys, tile visibility, skip decisions) then
+// lives in scalar registers and branches on it are uniform, instead of being
+// treated as per-lane values with exec-mask control flow.
+__device__ __forceinline__ int wave_id(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+
 }  // namespace attn
