@@ -78,26 +78,30 @@ def visible_pairs(mask: str, window: int, nq: int, nk: int) -> int:
     return int((hi - lo).sum())
 
 
-def kernel_work(w, pairs_per_bh: int) -> dict:
+def kernel_work(w, pairs_per_bh: int, kept_ds: bool = False) -> dict:
     """Algorithmic flops and compulsory HBM bytes per launch of each kernel.
 
     flops per visible pair: fwd 4 d (Q K^T and P V); dK/dV pass 8 d (S, dP,
-    dV, dK); dQ pass 2 d (the dQ product; its recomputed S and dP are not
-    credited), so the backward totals 10 d, which is also what the fused
-    single-tile backward is credited with.  Bytes: every tensor the kernel
-    must read or write, once."""
+    dV, dK); dQ pass 2 d (the dQ product; when it recomputes S and dP those
+    are not credited), so the backward totals 10 d, which is also what the
+    fused single-tile backward is credited with.  Bytes: every tensor the
+    kernel must read or write, once.  With ``kept_ds`` the dK/dV pass also
+    writes dS (bf16, 2 bytes per visible pair) and the dQ pass reads dS and K
+    only, instead of Q, dO, lse, D, K and V."""
     es = 2 if w.dtype == "bf16" else 4
     bh = w.B * w.H
     q_rows, k_rows, d = bh * w.Nq, bh * w.Nk, w.d
     pairs = bh * pairs_per_bh
+    ds_bytes = 2 * pairs if kept_ds else 0
+    dq_bytes = ((q_rows * d + k_rows * d) * es + ds_bytes if kept_ds
+                else (3 * q_rows * d + 2 * k_rows * d) * es + 8 * q_rows)
     return {
         "fwd": dict(flops=4 * d * pairs,
                     bytes=(2 * q_rows * d + 2 * k_rows * d) * es + 4 * q_rows),
         "rowsum": dict(flops=2 * d * q_rows, bytes=2 * q_rows * d * es + 4 * q_rows),
         "dkdv": dict(flops=8 * d * pairs,
-                     bytes=(2 * q_rows * d + 4 * k_rows * d) * es + 8 * q_rows),
-        "dq": dict(flops=2 * d * pairs,
-                   bytes=(3 * q_rows * d + 2 * k_rows * d) * es + 8 * q_rows),
+                     bytes=(2 * q_rows * d + 4 * k_rows * d) * es + 8 * q_rows + ds_bytes),
+        "dq": dict(flops=2 * d * pairs, bytes=dq_bytes),
         # the fused single-tile backward: reads Q, K, V, dO, lse, writes dQ,
         # dK, dV (its row sums come from P and dP in-tile, O is not read)
         "bwd": dict(flops=10 * d * pairs,
@@ -234,8 +238,11 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(attn.binding.workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8,
-                     device=dev)
+    # the larger workspace where it applies: the dQ pass then reads dS kept by
+    # the dK/dV pass instead of recomputing S and dP
+    ws_bytes = attn.binding.workspace_bytes_ds(q, k, mask=w.mask, window=w.window)
+    kept_ds = ws_bytes > attn.binding.workspace_bytes(w.B, w.H, w.Nq)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     kw = dict(mask=w.mask, window=w.window, scale=w.scale)
 
     fused = attn.binding.bwd_fused(q, k, v, mask=w.mask, window=w.window)
@@ -292,7 +299,7 @@ def main() -> int:
     pairs = pairs_bh * w.B * w.H
     flops_step = 14 * w.d * pairs
     value = flops_step / (ms_per_step * 1e-3) / 1e12
-    work = kernel_work(w, pairs_bh)
+    work = kernel_work(w, pairs_bh, kept_ds)
     dom = max(kernels, key=lambda kn: kern_ms[kn])
     wk = work[dom]
     ai = wk["flops"] / wk["bytes"]
@@ -336,8 +343,11 @@ def main() -> int:
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
            "mask": w.mask, "window": w.window, "dtype": w.dtype,
            "visible_pairs": pairs,
+           "workspace_bytes": ws_bytes,
            "step": ("attn_fwd + attn_bwd (one fused kernel: dK/dV and dQ waves side by side)"
-                    if fused else "attn_fwd + attn_bwd (row sums, dK/dV, dQ passes)")}
+                    if fused else
+                    "attn_fwd + attn_bwd (row sums, dK/dV keeping dS, dQ = scale dS K)"
+                    if kept_ds else "attn_fwd + attn_bwd (row sums, dK/dV, dQ passes)")}
     rec = {
         "metric": "attention fwd+bwd TFLOP/s at 1 MI355X; % of bf16 MFMA peak",
         "value": round(value, 3),

@@ -55,6 +55,9 @@ def load_library():
     lib.attn_bwd_fused.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_size_ds.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64,
+                                               ctypes.c_int, i64]
+    lib.attn_bwd_workspace_size_ds.restype = ctypes.c_size_t
     lib.attn_check_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_float,
                                    ctypes.c_int, i64, vp, vp, vp, vp, fp]
     lib.attn_check_fwd.restype = ctypes.c_int
@@ -118,22 +121,35 @@ def bwd_fused(q, k, v, mask: str = "none", window: int = 0) -> bool:
 
 
 def workspace_bytes(B: int, H: int, Nq: int) -> int:
+    """Minimum backward workspace (row sums only)."""
     return int(load_library().attn_bwd_workspace_size(B, H, Nq))
+
+
+def workspace_bytes_ds(q, k, mask: str = "none", window: int = 0) -> int:
+    """Backward workspace with which the dQ pass reads dS kept by the dK/dV
+    pass (``attn_bwd_workspace_size_ds``); equals ``workspace_bytes`` where
+    that path does not apply."""
+    B, H, Nq, d = q.shape
+    return int(load_library().attn_bwd_workspace_size_ds(
+        DTYPE_CODES[q.dtype], B, H, Nq, k.shape[2], d, MASK_CODES[mask], int(window)))
 
 
 PASS_ROWSUM, PASS_DKDV, PASS_DQ, PASS_ALL = 1, 2, 4, 7
 
 
 def bwd(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
-        workspace=None, dq=None, dk=None, dv=None, passes: int = PASS_ALL):
+        workspace=None, dq=None, dk=None, dv=None, passes: int = PASS_ALL,
+        keep_ds: bool = True):
     """dQ, dK, dV of attention given dO.  Returns tensors shaped like q, k, v.
     ``passes`` (a set of PASS_* bits) restricts the call to some of the
-    backward passes (``attn_bwd_passes``); the default runs all three."""
+    backward passes (``attn_bwd_passes``); the default runs all three.  When
+    no workspace is given one is allocated: with ``keep_ds`` large enough
+    for the dQ pass to read dS kept by the dK/dV pass, else the minimum."""
     lib = load_library()
     B, H, Nq, Nk, d = _geometry(q, k, v)
     if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, Nq):
         raise ValueError("o/do must match q and lse must be [B, H, Nq]")
-    ws_need = workspace_bytes(B, H, Nq)
+    ws_need = workspace_bytes_ds(q, k, mask, window) if keep_ds else workspace_bytes(B, H, Nq)
     if workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq

@@ -115,6 +115,29 @@ attn::MaskGeom make_geom(int mask, int64_t Nq, int64_t Nk, int64_t window) {
   return g;
 }
 
+// The dK/dV pass keeps dS for the dQ pass (bf16, general kernels, d = 128):
+// B * H * ds_blocks() blocks of 32 x 32 bf16 after the row sums.
+bool ds_applies(int dtype, int64_t d, const attn::MaskGeom& g) {
+  return dtype == ATTN_BF16 && d == 128 && !g.local64();
+}
+
+size_t ds_ws_size(int64_t B, int64_t H, int64_t Nq, const attn::MaskGeom& g) {
+  return ws_size(B, H, Nq) + (size_t)B * (size_t)H * (size_t)g.ds_blocks() *
+                                 (size_t)attn::kDsBlockElems * sizeof(uint16_t);
+}
+
+// bytes of the workspace a backward call uses: with room for the dS blocks
+// (where they apply) the dS path, else the row sums only
+size_t ws_used(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int mask,
+               int64_t window, size_t workspace_bytes) {
+  const attn::MaskGeom g = make_geom(mask, Nq, Nk, window);
+  if (ds_applies(dtype, d, g)) {
+    const size_t full = ds_ws_size(B, H, Nq, g);
+    if (workspace_bytes >= full) return full;
+  }
+  return ws_size(B, H, Nq);
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,11 +167,19 @@ int attn_check_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int6
   const Span ins[6] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}};
   if (!workspace) return ATTN_ERR_WORKSPACE;
   if (workspace_bytes < ws_size(B, H, Nq)) return ATTN_ERR_WORKSPACE;
-  const Span outs[4] = {{dq, qb}, {dk, kb}, {dv, kb}, {workspace, ws_size(B, H, Nq)}};
+  const Span outs[4] = {{dq, qb}, {dk, kb}, {dv, kb},
+                        {workspace, ws_used(dtype, B, H, Nq, Nk, d, mask, window, workspace_bytes)}};
   return check_buffers(ins, 6, outs, 4);
 }
 
 size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq) { return ws_size(B, H, Nq); }
+
+size_t attn_bwd_workspace_size_ds(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                  int64_t d, int mask, int64_t window) {
+  if (check_geometry(dtype, B, H, Nq, Nk, d, 1.0f, mask, window) != ATTN_OK) return 0;
+  const attn::MaskGeom g = make_geom(mask, Nq, Nk, window);
+  return ds_applies(dtype, d, g) ? ds_ws_size(B, H, Nq, g) : ws_size(B, H, Nq);
+}
 
 int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int mask,
                    int64_t window) {
@@ -212,6 +243,12 @@ int attn_bwd_passes(int passes, int dtype, int64_t B, int64_t H, int64_t Nq, int
   a.nk = (int)Nk;
   a.scale = scale;
   a.mg = make_geom(mask, Nq, Nk, window);
+  a.ds = nullptr;
+  a.ds_per_bh = 0;
+  if (ws_used(dtype, B, H, Nq, Nk, d, mask, window, workspace_bytes) > ws_size(B, H, Nq)) {
+    a.ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ws_size(B, H, Nq));
+    a.ds_per_bh = a.mg.ds_blocks();
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int err = dtype == ATTN_BF16 ? attn::launch_bwd_bf16(a, (int)d, s, passes)
                                      : attn::launch_bwd_fp32(a, (int)d, s, passes);

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // one key tile [j0, j0 + BN) from LDS: scores, online softmax, O += P V
   auto tile = [&](const uint16_t* k_l, const uint16_t* v_l, int j0) {
-    if (!(j0 < whi && j0 + BN > wlo)) return;
+    if (!(wlo < whi && j0 < whi && j0 + BN > wlo)) return;
     const bool full = mg.tile_full(wa, wb, j0, j0 + BN);
     f32x16 s[2];
 #pragma unroll
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const int ih = i0 + 32 * h;
-      if (!(ih < whi && ih + 32 > wlo)) continue;
+      if (!(wlo < whi && ih < whi && ih + 32 > wlo)) continue;
       f32x16 s[KB], dp[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -377,10 +377,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
 // in two roles working one query tile apart.
 //   score waves 0..3 (key block w): K, V rows of the block as register
 //     operands; per 32-query tile S = Q K^T, dP = dO V^T, P = exp(S*scale -
-//     lse), dS = P (dP - D), rounded to bf16 and handed over through LDS in
-//     the accumulator's register order (16 bytes per lane per 16-row chunk);
+//     lse), dS = P (dP - D), rounded to bf16 and handed over through LDS (P in
+//     the accumulator's register order, 16 bytes per lane per 16-row chunk;
+//     dS as a plain [key][query] tile);
 //   accumulate waves 4..7 (key block w - 4): dV^T += dO^T P, dK^T += Q^T dS
-//     with dO^T, Q^T from transpose reads of the same Q / dO tiles.
+//     with dO^T, Q^T from transpose reads of the same Q / dO tiles; when the
+//     caller gave room they also write each dS tile to the workspace for the
+//     dQ pass (the score waves carry the longer dependency chain per step).
 // Each role's live registers stay under the two-waves-per-SIMD budget, and
 // a score wave's softmax arithmetic overlaps its partner's MFMAs.  Q / dO
 // tiles cycle through three named buffers (one being loaded, one read by the
@@ -435,25 +438,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int r0 = t0 + j * BQ;
     rq.load(Q, r0, a.nq, tid);
     rg.load(dO, r0, a.nq, tid);
-    if (tid < 64) {
-      const float x = (tid < 32 ? LSE : DS)[min(r0 + (tid & 31), a.nq - 1)];
-      rstat = tid < 32 ? x * kLog2e : x;  // lse in log2 units
-    }
+    // every lane loads (no branch around a load: a value loaded under a
+    // divergent branch is waited for where the branch rejoins, which would
+    // cancel the prefetch); only threads 0..63 store theirs
+    const int t = tid & 63;
+    rstat = (t < 32 ? LSE : DS)[min(r0 + (t & 31), a.nq - 1)];
   };
   auto put = [&](uint16_t* q_l, uint16_t* g_l, float* s_l) {
     rq.store(q_l, tid);
     rg.store(g_l, tid);
-    if (tid < 64) s_l[tid] = rstat;
+    if (tid < 64) s_l[tid] = tid < 32 ? rstat * kLog2e : rstat;  // lse in log2 units
   };
   // put tile j into a set and fetch tile j + 1 into the registers
   auto load = [&](uint16_t* q_l, uint16_t* g_l, float* s_l, int j) {
     put(q_l, g_l, s_l);
     if (j + 1 < ntiles) fetch(j + 1);
   };
-  // does this wave's key block see any row of tile j
+  // does this wave's key block see any row of tile j (an empty query range
+  // [wlo, whi) sees none)
   auto sees = [&](int j) {
     const int i0 = t0 + j * BQ;
-    return i0 < whi && i0 + BQ > wlo;
+    return wlo < whi && i0 < whi && i0 + BQ > wlo;
   };
   const int hoff = (kb * 2 * 64 + lane) * 8;  // this lane's 16 bytes of chunk 0 in a P / dS buffer
 
@@ -501,10 +506,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
           dp[e] = p * (dp[e] - D4[jj]);
         }
       }
+      // P in register order; dS as a plain [key][query] 32 x 32 tile
+      uint16_t* dt = d_l + kb * 1024;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         *reinterpret_cast<bf16x8*>(p_l + hoff + c * 512) = acc_chunk(s, c);
-        *reinterpret_cast<bf16x8*>(d_l + hoff + c * 512) = acc_chunk(dp, c);
+        const bf16x8 v = acc_chunk(dp, c);
+        *reinterpret_cast<bf16x4*>(dt + (lane & 31) * 32 + 16 * c + 4 * gq) =
+            bf16x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<bf16x4*>(dt + (lane & 31) * 32 + 16 * c + 8 + 4 * gq) =
+            bf16x4{v[4], v[5], v[6], v[7]};
       }
     };
 
@@ -540,13 +551,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       dkacc[db] = f32x16{};
       dvacc[db] = f32x16{};
     }
+    // kept dS blocks of this key block: the (b, h) base plus the blocks of
+    // the key blocks before it
+    uint16_t* dsb = a.ds;
+    int64_t ds0 = 0;
+    if (a.ds) {
+      dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
+      ds0 = ds_offset(mg, wk0 / 32, lane);
+    }
     auto consume = [&](const uint16_t* q_l, const uint16_t* g_l, const uint16_t* p_l,
                        const uint16_t* d_l, int j) {
       if (!sees(j)) return;
+      if (a.ds) {
+        // keep the block for the dQ pass, already in its MFMA operand order
+        // (lane = query, 8 keys of a 16-key chunk per lane): 2 x 1 KB.  Block
+        // i0 / 32 - wlo / 32 of this key block's ds_count(): in range because
+        // sees(j) holds (a nonempty query range overlapping the tile).
+        const int i0 = t0 + j * BQ;
+        uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          *reinterpret_cast<bf16x8*>(blk + (cc * 64 + lane) * 8) =
+              lds_tr8_plain(d_l + kb * 1024, 32, 16 * cc, 0, lane);
+      }
+      const uint16_t* dt = d_l + kb * 1024 + (lane & 31) * 32;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 pop = *reinterpret_cast<const bf16x8*>(p_l + hoff + c * 512);
-        const bf16x8 dsop = *reinterpret_cast<const bf16x8*>(d_l + hoff + c * 512);
+        const bf16x4 d0 = *reinterpret_cast<const bf16x4*>(dt + 16 * c + 4 * gq);
+        const bf16x4 d1 = *reinterpret_cast<const bf16x4*>(dt + 16 * c + 8 + 4 * gq);
+        const bf16x8 dsop = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           dvacc[db] = mfma32(lds_tr8<D>(g_l, 16 * c, 32 * db, lane), pop, dvacc[db]);
@@ -589,6 +623,99 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     store_tile<32, D, 256>(dV, k0 + 64, a.nk, sQ1, tid - 256);
     store_tile<32, D, 256>(dV, k0 + 96, a.nk, sG1, tid - 256);
   }
+}
+
+// dQ pass from the kept dS blocks: dQ^T += K^T dS^T, nothing recomputed.
+// Workgroup = 4 waves x 32 query rows; K tiles of 128 keys double-buffered in
+// LDS (transpose reads give K^T), each wave's dS operands (16 bytes per lane
+// per 16-key chunk, stored by the dK/dV pass in exactly this register order)
+// loaded from the workspace one key tile ahead.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_ds_kernel(BwdArgs a, int nqt) {
+  constexpr int NT = 256, BM = 128, BN = 128, TE = tile_elems<BN, D>();
+  constexpr int DB = D / 32, NKB = BN / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TE];
+
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
+  const int wave = wave_id(tid);
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
+  MaskGeom mg = a.mg;
+  if (MODE != kAnyMask) mg.mode = MODE;
+  const int i0 = qt * BM, i1 = min(i0 + BM, a.nq);
+  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
+  const uint16_t* DS = a.ds + (int64_t)bh * a.ds_per_bh * kDsBlockElems;
+
+  const int wa = i0 + wave * 32;
+  const int jq = wa / 32;  // this wave's query block
+  int lo, hi;
+  mg.key_range(i0, i1, &lo, &hi);
+  const int t0 = (lo / BN) * BN;
+
+  // running block cursor: index of key block `kbn`'s first dS block
+  int kbn = t0 / 32;
+  int64_t cur = lo < hi ? ds_offset(mg, kbn, lane) : 0;
+  // operands of the 4 key blocks of one tile; bit kb of the mask: block kb
+  // has this wave's query block
+  auto fetch = [&](bf16x8 (&op)[NKB][2], unsigned& valid) {
+    valid = 0;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int jlo = mg.ds_jlo(kbn), cnt = mg.ds_count(kbn);
+      if (wa < a.nq && jq >= jlo && jq < jlo + cnt) {
+        const uint16_t* blk = DS + (cur + (jq - jlo)) * kDsBlockElems;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          op[kb][cc] = *reinterpret_cast<const bf16x8*>(blk + (cc * 64 + lane) * 8);
+        valid |= 1u << kb;
+      }
+      cur += cnt;
+      ++kbn;
+    }
+  };
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
+  auto tile = [&](const uint16_t* k_l, const bf16x8 (&op)[NKB][2], unsigned valid) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (!(valid & (1u << kb))) continue;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqacc[db] = mfma32(lds_tr8<D>(k_l, 32 * kb + 16 * cc, 32 * db, lane), op[kb][cc], dqacc[db]);
+    }
+  };
+
+  if (lo < hi) {
+    bf16x8 opA[NKB][2], opB[NKB][2];
+    unsigned vA = 0, vB = 0;
+    dma_tile<BN, D, NT>(sK0, K, t0, a.nk, tid);
+    fetch(opA, vA);
+    __syncthreads();
+    for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
+      if (j0 + BN < hi) {
+        dma_tile<BN, D, NT>(sK1, K, j0 + BN, a.nk, tid);
+        fetch(opB, vB);
+      }
+      tile(sK0, opA, vA);
+      __syncthreads();
+      if (j0 + BN >= hi) break;
+      if (j0 + 2 * BN < hi) {
+        dma_tile<BN, D, NT>(sK0, K, j0 + 2 * BN, a.nk, tid);
+        fetch(opA, vA);
+      }
+      tile(sK1, opB, vB);
+      __syncthreads();
+    }
+  }
+  acc_to_lds<D>(sK0, 32 * wave + (lane & 31), dqacc, a.scale, gq);
+  __syncthreads();
+  store_tile<BM, D, NT>((uint16_t*)a.dq + (int64_t)bh * a.nq * D, i0, a.nq, sK0, tid);
 }
 
 // ------------------------------------------------------------ backward: dQ
@@ -646,7 +773,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // one key tile [j0, j0 + BN): S^T, dP^T, dS^T per 32-key half (packed to
   // bf16 right away to keep the live set small), then dQ^T += K^T dS^T
   auto tile = [&](const uint16_t* k_l, const uint16_t* v_l, int j0) {
-    if (!(j0 < whi && j0 + BN > wlo)) return;
+    if (!(wlo < whi && j0 < whi && j0 + BN > wlo)) return;
     const bool full = mg.tile_full(wa, wb, j0, j0 + BN);
     bf16x8 dsop[BN / 16];
 #pragma unroll
@@ -736,8 +863,17 @@ int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
   }
   if (passes & kPassDQ) {
     const int nqt = (a.nq + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((dq_bf16_kernel<D, NW, MODE>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
-                       dim3(NW * 64), 0, s, a, nqt);
+    bool done = false;
+    if constexpr (D == 128) {
+      if (a.ds) {
+        hipLaunchKernelGGL((dq_ds_kernel<D, MODE>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
+                           dim3(256), 0, s, a, nqt);
+        done = true;
+      }
+    }
+    if (!done)
+      hipLaunchKernelGGL((dq_bf16_kernel<D, NW, MODE>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
+                         dim3(NW * 64), 0, s, a, nqt);
     if ((err = (int)hipGetLastError())) return err;
   }
   return 0;

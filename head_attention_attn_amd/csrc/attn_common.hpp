@@ -87,7 +87,39 @@ struct MaskGeom {
     if (b > nq || j1 > nk) return false;
     return j0 >= row_lo(b - 1) && j1 <= row_hi(a);
   }
+
+  // dS blocks kept by the backward for its dQ pass: one 32 x 32 block per
+  // (key block kb = keys 32 kb .. 32 kb + 31, query block jb = rows 32 jb ..
+  // 32 jb + 31) pair that has a visible entry.  The query blocks of key block
+  // kb that do are the contiguous range [ds_jlo(kb), ds_jlo(kb) + ds_count(kb)).
+  ATTN_HD void ds_rows(int kb, int* lo, int* hi) const {
+    const int a = 32 * kb;
+    if (a >= nk) {
+      *lo = *hi = 0;
+      return;
+    }
+    query_range(a, imin(a + 32, nk), lo, hi);
+  }
+  ATTN_HD int ds_jlo(int kb) const {
+    int lo, hi;
+    ds_rows(kb, &lo, &hi);
+    return lo / 32;
+  }
+  ATTN_HD int ds_count(int kb) const {
+    int lo, hi;
+    ds_rows(kb, &lo, &hi);
+    return lo < hi ? (hi + 31) / 32 - lo / 32 : 0;
+  }
+  // blocks per (b, h): the sum of ds_count over the key blocks
+  ATTN_HD int64_t ds_blocks() const {
+    int64_t n = 0;
+    for (int kb = 0; 32 * kb < nk; ++kb) n += ds_count(kb);
+    return n;
+  }
 };
+
+// elements of one dS block: 2 key chunks x 64 lanes x 8 bf16
+constexpr int kDsBlockElems = 1024;
 
 // ---------------------------------------------------------------- launches
 
@@ -113,6 +145,11 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsum;  // workspace: D_i = sum_c dO[i][c] * O[i][c], fp32 [B][H][Nq]
+  // optional workspace part: dS blocks written by the dK/dV pass and read by
+  // the dQ pass instead of recomputing S and dP (null: recompute);
+  // ds_per_bh = MaskGeom::ds_blocks() blocks per (b, h)
+  uint16_t* ds;
+  int64_t ds_per_bh;
   int B, H, nq, nk;
   float scale;
   MaskGeom mg;

@@ -123,6 +123,33 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, int
   }
 }
 
+// Transposed operand read of a plain row-major tile (row stride `stride`
+// elements, no swizzle): as lds_tr8 -- free index = column c0 + lane % 32,
+// contraction slots = rows r0 + 4g + e, r0 + 8 + 4g + e.
+__device__ __forceinline__ bf16x8 lds_tr8_plain(const uint16_t* tile, int stride, int r0, int c0,
+                                                int lane) {
+  const int grp = lane >> 4, li = lane & 15;
+  const int e = li >> 2, r = li & 3;
+  const int g = grp >> 1, half = grp & 1;
+  const uint16_t* p = tile + (r0 + 4 * g + e) * stride + c0 + 16 * half + 4 * r;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * stride));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Index of key block kb's first dS block within its (b, h): the sum of
+// ds_count over the key blocks before kb, summed by the 64 lanes of a wave
+// (lane l takes kb' = l, l + 64, ...); every lane returns the total.
+__device__ __forceinline__ int64_t ds_offset(const MaskGeom& mg, int kb, int lane) {
+  int64_t n = 0;
+  for (int k = lane; k < kb; k += 64) n += mg.ds_count(k);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m);
+  return n;
+}
+
 // Register-staged tile load: global -> registers now, registers -> LDS (in
 // the tile layout) later.  Unlike the direct-to-LDS load, a barrier between
 // the two does not wait for the global loads (a barrier waits for LDS

@@ -120,13 +120,32 @@ ATTN_API int attn_fwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, i
 ATTN_API size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
 
 /*
+ * attn_bwd_workspace_size_ds -- bytes of workspace with which attn_bwd keeps
+ * dS = P * (dP - D) (bf16) from its dK/dV pass for its dQ pass, so that the
+ * dQ pass is the plain product dQ = scale * dS K instead of recomputing S, P
+ * and dP (a choice of this library: the pages' backward designs either
+ * recompute or accumulate dQ with atomics).  The extra part holds one 32 x 32
+ * bf16 block (2 KB) per key block x query block pair with a visible entry,
+ * per (b, h): about 2 bytes per visible (query, key) pair, e.g. 1.35 GB for
+ * causal B=1, H=20, N=8192.  It applies to bf16, d = 128, and every mask
+ * except the block-local one of attn_bwd_fused(); elsewhere, and for any
+ * workspace smaller than this, attn_bwd recomputes and the value returned is
+ * attn_bwd_workspace_size(B, H, Nq).  Returns 0 for arguments attn_bwd would
+ * reject.  A caller short of memory may always pass the smaller size.
+ */
+ATTN_API size_t attn_bwd_workspace_size_ds(int dtype, int64_t B, int64_t H, int64_t Nq,
+                                           int64_t Nk, int64_t d, int mask, int64_t window);
+
+/*
  * attn_bwd -- backward pass: dQ, dK, dV of L given dO = dL/dO.
  *   q, k, v, o, lse  the forward inputs and outputs (o and lse as written by
  *                    attn_fwd for the same arguments)
  *   dout             dO, [B][H][Nq][d], dtype
  *   dq, dk, dv       device outputs, layouts of q, k, v
  *   workspace        device scratch of >= attn_bwd_workspace_size(B, H, Nq)
- *                    bytes, caller-owned; contents on entry are ignored
+ *                    bytes, caller-owned; contents on entry are ignored.  With
+ *                    >= attn_bwd_workspace_size_ds(...) bytes the dQ pass
+ *                    reads dS kept by the dK/dV pass (see there).
  * Other arguments as attn_fwd.  Three kernels run in stream order: the row-sum
  * pre-pass, the dK/dV pass (one workgroup per key tile, looping over visible
  * query tiles) and the dQ pass (one workgroup per query tile, looping over
@@ -176,9 +195,12 @@ ATTN_API int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t
  * and dQ passes read D from the workspace, so they need a row-sum pass with
  * the same o, dout and workspace earlier in stream order; once that pass is
  * done the two are independent of each other and a caller may enqueue them
- * on two streams (with an event from the row-sum pass's stream).  Passing a
- * workspace that holds no row sums gives wrong gradients, not a fault.  Use:
- * overlapping the two passes, and timing each pass on its own.
+ * on two streams (with an event from the row-sum pass's stream) -- except
+ * with a workspace of attn_bwd_workspace_size_ds() bytes where that exceeds
+ * attn_bwd_workspace_size(): then the dQ pass reads the dS blocks the dK/dV
+ * pass writes, and must follow it in stream order.  Passing a workspace that
+ * holds no row sums (or no dS blocks) gives wrong gradients, not a fault.
+ * Use: overlapping the passes, and timing each pass on its own.
  */
 ATTN_API int attn_bwd_passes(int passes, int dtype, int64_t B, int64_t H, int64_t Nq,
                              int64_t Nk, int64_t d, float scale, int mask, int64_t window,

@@ -36,11 +36,12 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def gpu_fwd_bwd(q, k, v, do, mask, window, scale):
+def gpu_fwd_bwd(q, k, v, do, mask, window, scale, keep_ds=True):
     dev = "cuda"
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
     o, lse = attn.fwd(qd, kd, vd, mask=mask, window=window, scale=scale)
-    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, mask=mask, window=window, scale=scale)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, mask=mask, window=window, scale=scale,
+                          keep_ds=keep_ds)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -75,14 +76,18 @@ def compare(name_vals, dtype, label="", tol=None, abs_only=(), amax_rel=0.0):
 
 
 def parity_case(B, H, Nq, Nk, d, dtype, mask, window=0, seed=0, scale=None, transform=None,
-                tol=None, abs_only=(), amax_rel=0.0):
-    """Full-tensor parity of one small case; returns the error report."""
+                tol=None, abs_only=(), amax_rel=0.0, keep_ds=True):
+    """Full-tensor parity of one small case; returns the error report.
+    ``keep_ds`` picks the backward workspace: large enough for the dQ pass to
+    read dS kept by the dK/dV pass (where that path applies), or the minimum
+    (dQ recomputes S and dP)."""
     scale = float(torch.tensor(1.0 / np.sqrt(d), dtype=torch.float32)) if scale is None else scale
-    say(f"[parity] B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype} mask={mask} W={window} seed={seed}")
+    say(f"[parity] B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype} mask={mask} W={window} seed={seed}"
+        f" keep_ds={keep_ds}")
     q, k, v, do = make_inputs(B, H, Nq, Nk, d, dtype, seed)
     if transform is not None:
         q, k, v, do = transform(q, k, v, do)
-    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, mask, window, scale)
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, mask, window, scale, keep_ds=keep_ds)
     ro, rl = oracle_fwd(to64(q), to64(k), to64(v), scale, mask, window)
     rdq, rdk, rdv = oracle_bwd(to64(q), to64(k), to64(v), to64(do), scale, mask, window)
     return compare([("O", to64(o), ro), ("lse", to64(lse), rl), ("dQ", to64(dq), rdq),

@@ -9,10 +9,12 @@ import subprocess
 import pytest
 
 from head_attention_attn_amd import binding
+from oracle.attention import visible
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, ALIAS, DEVICE, LAUNCH = range(8)
 BF16, FP32 = 0, 1
+MASK = {"none": 0, "causal": 1, "sliding": 2, "block": 3}
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +32,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_passes", "attn_bwd_fused",
-                                         "attn_bwd_workspace_size",
+                                         "attn_bwd_workspace_size", "attn_bwd_workspace_size_ds",
                                          "attn_check_fwd", "attn_check_bwd", "attn_status_string"])
 
 
@@ -58,6 +60,42 @@ def test_workspace_size(lib):
     assert lib.attn_bwd_workspace_size(1, 20, 8192) == 20 * 8192 * 4
     assert lib.attn_bwd_workspace_size(3, 1, 5) == 256
     assert lib.attn_bwd_workspace_size(0, 1, 5) == 0
+
+
+def _ds_blocks_from_visibility(mask, window, nq, nk):
+    """32 x 32 (key block, query block) pairs holding a visible entry, counted
+    from the oracle's visibility matrix."""
+    vis = visible(mask, window, nq, nk)
+    n = 0
+    for kb in range(0, nk, 32):
+        for jb in range(0, nq, 32):
+            n += bool(vis[jb:jb + 32, kb:kb + 32].any())
+    return n
+
+
+@pytest.mark.parametrize("nq,nk,mask,window", [
+    (128, 128, "causal", 0), (333, 333, "causal", 0), (200, 200, "none", 0),
+    (300, 300, "sliding", 70), (256, 256, "block", 128), (150, 40, "sliding", 16),
+    (37, 150, "causal", 0), (100, 37, "none", 0), (40, 150, "sliding", 16),
+])
+def test_workspace_size_ds_counts_visible_blocks(lib, nq, nk, mask, window):
+    """attn_bwd_workspace_size_ds = row sums + 2 KB per visible 32 x 32
+    block per (b, h), the blocks counted here independently of the library."""
+    B, H = 2, 3
+    base = lib.attn_bwd_workspace_size(B, H, nq)
+    got = lib.attn_bwd_workspace_size_ds(0, B, H, nq, nk, 128, MASK[mask], window)
+    assert got == base + B * H * _ds_blocks_from_visibility(mask, window, nq, nk) * 2048
+
+
+def test_workspace_size_ds_where_it_does_not_apply(lib):
+    base = lib.attn_bwd_workspace_size(1, 2, 256)
+    assert lib.attn_bwd_workspace_size_ds(0, 1, 2, 256, 256, 96, 1, 0) == base     # d != 128
+    assert lib.attn_bwd_workspace_size_ds(1, 1, 2, 256, 256, 128, 1, 0) == base    # fp32
+    assert lib.attn_bwd_workspace_size_ds(0, 1, 2, 256, 256, 128, 3, 64) == base   # fused block-local
+    assert lib.attn_bwd_workspace_size_ds(0, 1, 2, 256, 256, 128, 3, 5) == 0       # invalid window
+    # the causal N=8192, H=20 workload: 256 * 257 / 2 blocks per head
+    assert lib.attn_bwd_workspace_size_ds(0, 1, 20, 8192, 8192, 128, 1, 0) == \
+        lib.attn_bwd_workspace_size(1, 20, 8192) + 20 * (256 * 257 // 2) * 2048
 
 
 # Fake, never-dereferenced device addresses, far apart and 16-byte aligned.

@@ -60,3 +60,16 @@ def test_fused_backward_bytes():
     wk = bench.kernel_work(b, 49 * 64 * 64)["bwd"]
     assert wk["bytes"] == rows * (7 * b.d * 2 + 4)
     assert wk["flops"] == 10 * b.d * 49 * 64 * 64 * b.B * b.H
+
+
+def test_kept_ds_bytes():
+    """With dS kept: the dK/dV pass writes 2 bytes per visible pair more, and
+    the dQ pass reads dS and K and writes dQ (no Q, dO, lse, D, V)."""
+    w = WORKLOADS["causal_lm"]
+    pairs = bench.visible_pairs(w.mask, w.window, w.Nq, w.Nk) * w.B * w.H
+    rows = w.B * w.H * w.Nq
+    plain = bench.kernel_work(w, pairs // (w.B * w.H))
+    kept = bench.kernel_work(w, pairs // (w.B * w.H), kept_ds=True)
+    assert kept["dkdv"]["bytes"] == plain["dkdv"]["bytes"] + 2 * pairs
+    assert kept["dq"]["bytes"] == rows * w.d * 2 * 2 + 2 * pairs
+    assert kept["dq"]["flops"] == plain["dq"]["flops"]

@@ -32,6 +32,46 @@ def test_bf16_ragged_multi_tile(d, mask, window):
     parity_case(2, 2, n, n, d, "bf16", mask, window, seed=1)
 
 
+@pytest.mark.parametrize("keep_ds", [True, False])
+@pytest.mark.parametrize("nq,nk,mask,window", [
+    (200, 200, "none", 0), (333, 333, "causal", 0), (300, 300, "sliding", 70),
+    (256, 256, "block", 128),          # block mask on the general path (w does not divide 64)
+    (150, 40, "sliding", 16), (37, 150, "causal", 0), (100, 37, "none", 0),
+])
+def test_bf16_d128_both_dq_paths(keep_ds, nq, nk, mask, window):
+    """d = 128, the size where the dK/dV pass can keep dS for the dQ pass:
+    with the larger workspace (dQ = scale * dS K from the kept blocks) and
+    with the minimum one (dQ recomputes S and dP), each against the oracle,
+    on shapes with partial key and query blocks, empty rows and Nq != Nk."""
+    parity_case(2, 2, nq, nk, 128, "bf16", mask, window, seed=12, keep_ds=keep_ds)
+
+
+@pytest.mark.parametrize("B,H,nq,nk,mask,window", [
+    (1, 3, 260, 260, "causal", 0),
+    # key blocks whose query range is empty (keys no row can see): they keep no block
+    (2, 2, 37, 150, "causal", 0), (2, 2, 150, 40, "sliding", 16), (2, 2, 40, 150, "sliding", 16),
+])
+def test_kept_ds_workspace_guard_bands(B, H, nq, nk, mask, window):
+    """The dS blocks land inside the workspace attn_bwd_workspace_size_ds
+    asks for: guard bands on both sides stay untouched, and the result equals
+    the recomputing path's within the bf16 tolerance."""
+    d = 128
+    say(f"[ds guard] {mask} W={window} bf16 d=128 B={B} H={H} Nq={nq} Nk={nk}")
+    q, k, v, do = (t.cuda() for t in make_inputs(B, H, nq, nk, d, "bf16", seed=13))
+    o, lse = attn.fwd(q, k, v, mask=mask, window=window)
+    need = attn.binding.workspace_bytes_ds(q, k, mask=mask, window=window)
+    assert need > attn.binding.workspace_bytes(B, H, nq)
+    G = 1 << 16
+    buf = torch.full((need + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = attn.bwd(q, k, v, o, lse, do, mask=mask, window=window,
+                          workspace=buf[G:G + need])
+    dq2, dk2, dv2 = attn.bwd(q, k, v, o, lse, do, mask=mask, window=window, keep_ds=False)
+    torch.cuda.synchronize()
+    assert bool((buf[:G] == 0xA5).all()) and bool((buf[G + need:] == 0xA5).all())
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        compare([("x", to64(a), to64(b))], "bf16", "ds vs recompute")
+
+
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 5)])
 def test_fp32_ragged(d, mask, window):
