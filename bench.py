@@ -209,6 +209,9 @@ def main() -> int:
     ap.add_argument("--workload", default="block_local_hiera")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline (0 skips it)")
+    ap.add_argument("--autograd-steps", type=int, default=20,
+                    help="after the timed region, time this many steps through the "
+                         "torch.autograd wrapper (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run a plain device copy of this "
                          "many MiB 5 times (a known-size reference for HBM counters)")
@@ -283,6 +286,31 @@ def main() -> int:
                for i, kn in enumerate(kernels)}
     log(f"[bench] {ms_per_step:.4f} ms/step; per kernel (ms): "
         + ", ".join(f"{kn} {kern_ms[kn]:.4f}" for kn in kernels))
+
+    # the same step through the autograd wrapper (forward, then backward from
+    # dO by torch.autograd.grad), timed on its own after the main region
+    autograd_rec = None
+    if args.autograd_steps > 0:
+        qa, ka, va = (t.detach().requires_grad_(True) for t in (q, k, v))
+
+        def ag_step():
+            oa = attn.fused_attention(qa, ka, va, w.mask, w.window, w.scale)
+            return torch.autograd.grad(oa, (qa, ka, va), do)
+
+        for _ in range(3):
+            ag_step()
+        torch.cuda.synchronize(dev)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(args.autograd_steps):
+            ag_step()
+        a1.record()
+        torch.cuda.synchronize(dev)
+        ag_ms = a0.elapsed_time(a1) / args.autograd_steps
+        autograd_rec = {"ms_per_step": round(ag_ms, 5), "steps": args.autograd_steps,
+                        "over_direct_calls": round(ag_ms / ms_per_step, 4)}
+        log(f"[bench] autograd wrapper: {ag_ms:.4f} ms/step")
+        del qa, ka, va
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -367,6 +395,7 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,
+        "autograd": autograd_rec,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count, "torch": torch.__version__,
                    "hip": torch.version.hip},

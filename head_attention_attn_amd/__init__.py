@@ -6,5 +6,7 @@ entry points.  The library is loaded on first use and its absence is an error:
 there is no fallback path.
 """
 from .binding import fwd, bwd, lib_path, load_library, AttnError, MASK_CODES
+from .autograd import FusedAttention, FusedAttentionFunction, fused_attention
 
-__all__ = ["fwd", "bwd", "lib_path", "load_library", "AttnError", "MASK_CODES"]
+__all__ = ["fwd", "bwd", "lib_path", "load_library", "AttnError", "MASK_CODES",
+           "FusedAttention", "FusedAttentionFunction", "fused_attention"]

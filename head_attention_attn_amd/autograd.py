@@ -1,0 +1,73 @@
+"""torch.autograd bridge over the C ABI: the fused attention as a
+differentiable op and as an ``nn.Module``.
+
+The forward calls ``attn_fwd`` and saves O and the per-row logsumexp; the
+backward calls ``attn_bwd`` with them and the incoming dO.  This is how the
+pages put fused attention kernels under a model: "IHA-CUDA" (End-to-End
+Training Benchmark) has its baseline attention layer call the forward and
+backward kernels through a ``torch.autograd.Function`` wrapper, and
+"hiera-optim 0.1.0" (sdist ``hiera_optim/attention/mask_unit.py``,
+``MaskUnitAttentionFast``) is an ``nn.Module`` whose attention core takes
+q, k, v of shape [batch, heads, tokens, head_dim] and returns O of that
+shape.  Nothing here does arithmetic on the tensors: shapes are
+checked, contiguous inputs are required, and every product and softmax runs
+in the library's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding
+
+
+class FusedAttentionFunction(torch.autograd.Function):
+    """O = softmax(scale * Q K^T + mask) V, with dQ, dK, dV from ``attn_bwd``.
+
+    Inputs: contiguous device tensors q [B, H, Nq, d], k and v [B, H, Nk, d]
+    (bf16 or fp32), the mask name, its window and the scale (None: d^-0.5).
+    Returns O [B, H, Nq, d].  ``keep_ds`` picks the backward workspace: large
+    enough for the dQ pass to read dS kept by the dK/dV pass where that path
+    applies (``attn_bwd_workspace_size_ds``), else the minimum."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask="none", window=0, scale=None, keep_ds=True):
+        o, lse = binding.fwd(q, k, v, mask=mask, window=window, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (mask, window, scale, keep_ds)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        mask, window, scale, keep_ds = ctx.cfg
+        # the kernels read dO as a contiguous [B, H, Nq, d] tensor of q's dtype
+        do = do.to(q.dtype).contiguous()
+        dq, dk, dv = binding.bwd(q, k, v, o, lse, do, mask=mask, window=window, scale=scale,
+                                 keep_ds=keep_ds)
+        return dq, dk, dv, None, None, None, None
+
+
+def fused_attention(q, k, v, mask: str = "none", window: int = 0, scale=None,
+                    keep_ds: bool = True):
+    """Differentiable fused attention (see ``FusedAttentionFunction``)."""
+    return FusedAttentionFunction.apply(q, k, v, mask, window, scale, keep_ds)
+
+
+class FusedAttention(torch.nn.Module):
+    """The attention core of a transformer layer as a module: no parameters;
+    ``forward(q, k, v)`` with q [B, H, Nq, d], k, v [B, H, Nk, d] returns O
+    [B, H, Nq, d].  ``mask`` is "none", "causal", "sliding" (``window`` keys
+    including the diagonal) or "block" (independent windows of ``window``
+    tokens, the mask-unit case); ``scale`` defaults to d^-0.5."""
+
+    def __init__(self, mask: str = "none", window: int = 0, scale=None, keep_ds: bool = True):
+        super().__init__()
+        if mask not in binding.MASK_CODES:
+            raise ValueError(f"unknown mask {mask!r}")
+        self.mask, self.window, self.scale, self.keep_ds = mask, int(window), scale, keep_ds
+
+    def forward(self, q, k, v):
+        return fused_attention(q, k, v, self.mask, self.window, self.scale, self.keep_ds)
+
+    def extra_repr(self) -> str:
+        return f"mask={self.mask!r}, window={self.window}, scale={self.scale}"

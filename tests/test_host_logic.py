@@ -22,3 +22,11 @@ def test_tile_ranges_against_brute_force(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().endswith("0 failures")
+
+
+def test_attention_module_rejects_unknown_mask():
+    import pytest
+    import head_attention_attn_amd as attn
+    with pytest.raises(ValueError):
+        attn.FusedAttention(mask="diagonal")
+    assert "causal" in repr(attn.FusedAttention(mask="causal"))
