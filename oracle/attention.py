@@ -22,7 +22,12 @@ Readings where the pages are silent (each is listed in the design notes):
   to any gradient (dQ row = 0).
 * Causal and sliding masks are top-left aligned on absolute indices
   (key j visible to query i iff j <= i [and j > i - W]), also when Nq != Nk.
-* Block-local: query i and key j see each other iff floor(i/w) == floor(j/w).
+* Block-local: query i and key j see each other iff they fall in the same
+  window.  With Nq == Nk the windows are floor(i/w) == floor(j/w).  With
+  pooled queries (hiera-optim ``MaskUnitAttentionFast.forward`` with
+  ``q_stride > 1``: Q is max-pooled inside each window, so a window holds
+  T keys but only T / q_stride queries, and SDPA runs per window on those),
+  the Nk / w windows of w keys each hold Nq / (Nk / w) consecutive query rows.
 """
 from __future__ import annotations
 
@@ -39,7 +44,9 @@ def visible(mask: str, window: int, nq: int, nk: int, rows=None) -> np.ndarray:
     none    -> every key
     causal  -> j <= i
     sliding -> i - window < j <= i         (window >= 1 keys incl. the diagonal)
-    block   -> floor(i / window) == floor(j / window)
+    block   -> same window: floor(i / wq) == floor(j / window) with
+               nw = nk / window windows and wq = nq / nw query rows per
+               window (wq = window when nq == nk)
     """
     i = np.arange(nq) if rows is None else np.asarray(rows)
     i = i[:, None]
@@ -53,9 +60,12 @@ def visible(mask: str, window: int, nq: int, nk: int, rows=None) -> np.ndarray:
             raise ValueError("sliding window must be >= 1")
         return (j <= i) & (j > i - window)
     if mask == "block":
-        if window < 1:
-            raise ValueError("block length must be >= 1")
-        return (i // window) == (j // window)
+        if window < 1 or nk % window:
+            raise ValueError("block length must be >= 1 and divide nk")
+        nw = nk // window
+        if nq % nw:
+            raise ValueError("block mode needs nq divisible by the number of windows")
+        return (i // (nq // nw)) == (j // window)
     raise ValueError(f"unknown mask {mask!r}")
 
 

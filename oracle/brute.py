@@ -16,7 +16,10 @@ from __future__ import annotations
 import math
 
 
-def sees(mask: str, window: int, i: int, j: int) -> bool:
+def sees(mask: str, window: int, i: int, j: int, window_q: int = 0) -> bool:
+    """Is key j visible to query i.  block: query i lies in window
+    i // window_q (window_q query rows per window; default ``window``) and key
+    j in window j // window."""
     if mask == "none":
         return True
     if mask == "causal":
@@ -24,12 +27,13 @@ def sees(mask: str, window: int, i: int, j: int) -> bool:
     if mask == "sliding":
         return i - window < j <= i
     if mask == "block":
-        return i // window == j // window
+        return i // (window_q or window) == j // window
     raise ValueError(mask)
 
 
-def brute_fwd(q, k, v, scale, mask="none", window=0):
-    """q, k, v: nested lists [B][H][N][d] of floats.  Returns (o, lse) lists."""
+def brute_fwd(q, k, v, scale, mask="none", window=0, window_q=0):
+    """q, k, v: nested lists [B][H][N][d] of floats.  Returns (o, lse) lists.
+    ``window_q``: query rows per block window when queries are pooled."""
     B, H = len(q), len(q[0])
     o, lse = [], []
     for b in range(B):
@@ -38,7 +42,7 @@ def brute_fwd(q, k, v, scale, mask="none", window=0):
             oh, lh = [], []
             Q, K, V = q[b][h], k[b][h], v[b][h]
             for i in range(len(Q)):
-                js = [j for j in range(len(K)) if sees(mask, window, i, j)]
+                js = [j for j in range(len(K)) if sees(mask, window, i, j, window_q)]
                 if not js:
                     oh.append([0.0] * len(V[0]))
                     lh.append(-math.inf)

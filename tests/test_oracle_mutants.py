@@ -29,7 +29,9 @@ MUTANTS = {
                               "dv[b, h] += (p.T @ do[b, h, rows])[::-1]"),
     "causal_strict": ("        return j <= i\n", "        return j < i\n"),
     "sliding_off_by_one": ("return (j <= i) & (j > i - window)", "return (j <= i) & (j >= i - window)"),
-    "block_modulo": ("return (i // window) == (j // window)", "return (i % window) == (j % window)"),
+    "block_modulo": ("return (i // (nq // nw)) == (j // window)", "return (i % (nq // nw)) == (j % window)"),
+    "block_query_window_unpooled": ("return (i // (nq // nw)) == (j // window)",
+                                    "return (i // window) == (j // window)"),
     "lse_log2": ("m_safe + np.log(np.where(empty, 1.0, tot))", "m_safe + np.log2(np.where(empty, 1.0, tot))"),
     "scores_unscaled": ("s = scale * (q2 @ k2.T)", "s = (q2 @ k2.T)"),
     "transposed_scores": ("s = scale * (q2 @ k2.T)", "s = scale * (q2 @ k2.T)[:, ::-1]"),
@@ -49,16 +51,19 @@ def _pins_pass(ns) -> bool:
     rng = np.random.default_rng(5)
     fwd, bwd, vis = ns["oracle_fwd"], ns["oracle_bwd"], ns["visible"]
     try:
-        for mask, window in (("none", 0), ("causal", 0), ("sliding", 3), ("block", 4)):
+        for mask, window, nq in (("none", 0, 8), ("causal", 0, 8), ("sliding", 3, 8), ("block", 4, 8),
+                                 ("block", 4, 4)):
             n, d, scale = 8, 4, 0.7
-            q, k, v, do = (rng.standard_normal((1, 2, n, d)) for _ in range(4))
+            wq = nq // (n // window) if mask == "block" else 0
+            q, do = (rng.standard_normal((1, 2, nq, d)) for _ in range(2))
+            k, v = (rng.standard_normal((1, 2, n, d)) for _ in range(2))
             # brute force forward with an independent visibility rule
             o, lse = fwd(q, k, v, scale, mask, window)
-            ob, lb = brute_fwd(q.tolist(), k.tolist(), v.tolist(), scale, mask, window)
+            ob, lb = brute_fwd(q.tolist(), k.tolist(), v.tolist(), scale, mask, window, wq)
             if np.max(np.abs(o - np.array(ob))) > 1e-12 or np.max(np.abs(lse - np.array(lb))) > 1e-12:
                 return False
             # library routine with autograd; its mask built by the brute-force rule
-            m = torch.tensor([[sees(mask, window, i, j) for j in range(n)] for i in range(n)])
+            m = torch.tensor([[sees(mask, window, i, j, wq) for j in range(n)] for i in range(nq)])
             qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
             ot = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
             (ot * torch.tensor(do)).sum().backward()

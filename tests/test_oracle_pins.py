@@ -27,16 +27,40 @@ def rand(*shape, rng=RNG):
 
 # ---------------------------------------------------------------- visibility
 
+def _block_wq(window, nq, nk):
+    """Query rows per block window (None: the shape has no block layout)."""
+    if nk % window or nq % (nk // window):
+        return None
+    return nq // (nk // window)
+
+
 @pytest.mark.parametrize("mask,window", MASK_WINDOWS + [("sliding", 1), ("block", 1), ("sliding", 40)])
-@pytest.mark.parametrize("nq,nk", [(8, 8), (12, 12), (5, 9), (9, 5)])
+@pytest.mark.parametrize("nq,nk", [(8, 8), (12, 12), (5, 9), (9, 5), (6, 12), (3, 12), (4, 8)])
 def test_visibility_brute(mask, window, nq, nk):
-    if mask == "block" and (nq != nk or nk % window):
-        pytest.skip("block mode needs Nq == Nk divisible by the block")
+    wq = _block_wq(window, nq, nk) if mask == "block" else 0
+    if wq is None:
+        pytest.skip("block mode needs Nk divisible by the block and Nq by the window count")
     from oracle.brute import sees
     vis = visible(mask, window, nq, nk)
     for i in range(nq):
         for j in range(nk):
-            assert vis[i, j] == sees(mask, window, i, j)
+            assert vis[i, j] == sees(mask, window, i, j, wq)
+
+
+def test_block_rejects_shapes_without_windows():
+    for nq, nk, w in ((8, 8, 3), (5, 8, 4), (7, 12, 4)):
+        with pytest.raises(ValueError):
+            visible("block", w, nq, nk)
+
+
+def test_pooled_block_visibility_by_hand():
+    """Nk = 8 keys in windows of 4 (two windows), Nq = 4 pooled query rows:
+    rows 0, 1 belong to window 0 (keys 0..3), rows 2, 3 to window 1 (4..7)."""
+    want = np.array([[1, 1, 1, 1, 0, 0, 0, 0],
+                     [1, 1, 1, 1, 0, 0, 0, 0],
+                     [0, 0, 0, 0, 1, 1, 1, 1],
+                     [0, 0, 0, 0, 1, 1, 1, 1]], dtype=bool)
+    assert (visible("block", 4, 4, 8) == want).all()
 
 
 def test_visibility_special_cases():
@@ -88,13 +112,16 @@ def _read_golden_table(name):
 @pytest.mark.parametrize("mask,window", MASK_WINDOWS + [("sliding", 1)])
 @pytest.mark.parametrize("nq,nk,d", [(8, 8, 4), (6, 9, 3), (9, 6, 5)])
 def test_forward_vs_brute_force(mask, window, nq, nk, d):
-    if mask == "block" and (nq != nk or nk % window):
-        nq = nk = 8
+    wq = 0
+    if mask == "block":
+        # equal windows, then pooled queries: 4 query rows over 8 keys
+        nq, nk = {8: (8, 8), 6: (4, 8), 9: (2, 8)}[nq]
+        wq = nq // (nk // window)
     B, H = 2, 2
     q, k, v = rand(B, H, nq, d), rand(B, H, nk, d), rand(B, H, nk, d)
     scale = 0.7
     o, lse = oracle_fwd(q, k, v, scale, mask, window)
-    ob, lb = brute_fwd(q.tolist(), k.tolist(), v.tolist(), scale, mask, window)
+    ob, lb = brute_fwd(q.tolist(), k.tolist(), v.tolist(), scale, mask, window, wq)
     ob, lb = np.array(ob), np.array(lb)
     assert np.array_equal(np.isneginf(lse), np.isneginf(lb))
     fin = np.isfinite(lb)
@@ -281,6 +308,54 @@ def test_block_local_equals_dense_on_reshaped_windows():
     gw = oracle_bwd(to_windows(q), to_windows(k), to_windows(v), to_windows(do), 0.5, "none")
     for x, y in zip(g, gw):
         assert np.max(np.abs(to_windows(x) - y)) < 1e-13
+
+
+@pytest.mark.parametrize("nw,w,wq", [(3, 8, 2), (2, 4, 1), (4, 6, 3)])
+def test_pooled_block_equals_dense_on_reshaped_windows(nw, w, wq):
+    """hiera-optim MaskUnitAttentionFast with q_stride = w / wq: after the
+    query pooling each window is an independent dense SDPA of wq queries over
+    w keys.  Block-local with Nq = nw * wq, Nk = nw * w equals torch's float64
+    SDPA (and its autograd) run per window with windows folded into the batch."""
+    B, H, d, scale = 2, 2, 5, 0.45
+    q, do = rand(B, H, nw * wq, d), rand(B, H, nw * wq, d)
+    k, v = rand(B, H, nw * w, d), rand(B, H, nw * w, d)
+
+    def to_windows(x, t):
+        return x.reshape(B, H, nw, t, d).transpose(0, 2, 1, 3, 4).reshape(B * nw, H, t, d)
+
+    o, lse = oracle_fwd(q, k, v, scale, "block", w)
+    dq, dk, dv = oracle_bwd(q, k, v, do, scale, "block", w)
+    qt, kt, vt = (torch.tensor(to_windows(x, t), requires_grad=True)
+                  for x, t in ((q, wq), (k, w), (v, w)))
+    ot = F.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    (ot * torch.tensor(to_windows(do, wq))).sum().backward()
+    assert np.max(np.abs(to_windows(o, wq) - ot.detach().numpy())) < 1e-12
+    lse_t = torch.logsumexp(scale * (qt @ kt.transpose(-1, -2)), dim=-1).detach().numpy()
+    assert np.max(np.abs(lse.reshape(B, H, nw, wq).transpose(0, 2, 1, 3).reshape(B * nw, H, wq)
+                         - lse_t)) < 1e-12
+    for x, t, g in ((dq, wq, qt.grad), (dk, w, kt.grad), (dv, w, vt.grad)):
+        assert np.max(np.abs(to_windows(x, t) - g.numpy())) < 1e-11
+
+
+def test_pooled_block_backward_finite_differences():
+    """Pooled-query block mask (Nq = 4, Nk = 8, window 4): gradients of
+    sum(O * dO) against central differences."""
+    rng = np.random.default_rng(11)
+    q, do = rng.standard_normal((1, 1, 4, 3)), rng.standard_normal((1, 1, 4, 3))
+    k, v = rng.standard_normal((1, 1, 8, 3)), rng.standard_normal((1, 1, 8, 3))
+    grads = oracle_bwd(q, k, v, do, 0.8, "block", 4)
+    h = 1e-6
+    for which, g in enumerate(grads):
+        args = [q, k, v]
+        fd = np.zeros_like(args[which])
+        for idx in np.ndindex(fd.shape):
+            ap, am = [a.copy() for a in args], [a.copy() for a in args]
+            ap[which][idx] += h
+            am[which][idx] -= h
+            fp = np.sum(oracle_fwd(*ap, 0.8, "block", 4)[0] * do)
+            fm = np.sum(oracle_fwd(*am, 0.8, "block", 4)[0] * do)
+            fd[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(fd - g)) < 1e-7
 
 
 def test_key_value_permutation_invariance():
