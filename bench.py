@@ -22,7 +22,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              outside the timed region
 
 Workloads (``--workload``): block_local_hiera (default; Hiera-Base mask-unit
-attention, 49 windows of 64 tokens, B=128, d=96), global_vision, causal_lm,
+attention, 49 windows of 64 tokens, B=128, d=96), block_pooled_hiera (the
+same windows with 16 pooled query rows each, H=2), global_vision, causal_lm,
 sliding_pseudo_head, tiny_exact_fp32.  ``--gpus`` above 1 is refused: this
 path runs on one GPU.
 """
@@ -65,7 +66,9 @@ def row_intervals(mask: str, window: int, nq: int, nk: int):
     elif mask == "sliding":
         lo, hi = np.maximum(0, i - window + 1), np.minimum(i + 1, nk)
     elif mask == "block":
-        lo = (i // window) * window
+        # nk / window windows of `window` keys, nq / (nk / window) query rows each
+        wq = nq // (nk // window)
+        lo = (i // wq) * window
         hi = np.minimum(lo + window, nk)
     else:
         raise ValueError(mask)

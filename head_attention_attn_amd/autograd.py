@@ -58,7 +58,9 @@ class FusedAttention(torch.nn.Module):
     ``forward(q, k, v)`` with q [B, H, Nq, d], k, v [B, H, Nk, d] returns O
     [B, H, Nq, d].  ``mask`` is "none", "causal", "sliding" (``window`` keys
     including the diagonal) or "block" (independent windows of ``window``
-    tokens, the mask-unit case); ``scale`` defaults to d^-0.5."""
+    keys, the mask-unit case; each window holds Nq / (Nk / window) query rows,
+    fewer than ``window`` when queries are pooled); ``scale`` defaults to
+    d^-0.5."""
 
     def __init__(self, mask: str = "none", window: int = 0, scale=None, keep_ds: bool = True):
         super().__init__()

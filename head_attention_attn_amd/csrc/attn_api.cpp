@@ -55,7 +55,10 @@ int check_geometry(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int6
       if (window < 1 || window > kMaxSeq) return ATTN_ERR_INVALID_ARG;
       break;
     case ATTN_MASK_BLOCK:
-      if (window < 1 || Nq != Nk || Nk % window != 0) return ATTN_ERR_INVALID_ARG;
+      // Nk / window windows of `window` keys; each holds Nq / (Nk / window)
+      // query rows (fewer than `window` when queries are pooled)
+      if (window < 1 || window > Nk || Nk % window != 0) return ATTN_ERR_INVALID_ARG;
+      if (Nq % (Nk / window) != 0) return ATTN_ERR_INVALID_ARG;
       break;
     default:
       return ATTN_ERR_INVALID_ARG;
@@ -112,6 +115,7 @@ attn::MaskGeom make_geom(int mask, int64_t Nq, int64_t Nk, int64_t window) {
   g.nq = (int)Nq;
   g.nk = (int)Nk;
   g.window = (mask == ATTN_MASK_SLIDING || mask == ATTN_MASK_BLOCK) ? (int)window : 0;
+  g.window_q = mask == ATTN_MASK_BLOCK ? (int)(Nq / (Nk / window)) : 0;
   return g;
 }
 

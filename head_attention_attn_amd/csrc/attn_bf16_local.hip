@@ -1,24 +1,29 @@
 // attn_bf16_local.hip -- bf16 kernels for attention whose every query row sees
-// keys of its own 64-row tile only: block-local (mask-unit) attention with a
-// window that divides 64 ("hiera-optim 0.1.0" sdist, mask_unit.py,
+// keys of its own 64-key tile only: block-local (mask-unit) attention with a
+// key window w that divides 64 ("hiera-optim 0.1.0" sdist, mask_unit.py,
 // MaskUnitAttentionFast: tokens split into independent windows, dense softmax
-// attention inside each window).  Such attention is HBM-bound: a 64-token
-// window with d = 96 costs ~4 MFLOP of MFMA work against ~100 KB of HBM
-// traffic, so these kernels are built around moving each byte once.
+// attention inside each window), each window holding wq query rows with wq
+// dividing w -- wq = w, or fewer when the queries are max-pooled inside the
+// window (MaskUnitAttentionFast with q_stride = w / wq).  A tile is then 64
+// keys, i.e. 64 / w whole windows, and their QT = 64 wq / w query rows.  Such
+// attention is HBM-bound: a 64-token window with d = 96 costs ~4 MFLOP of
+// MFMA work against ~100 KB of HBM traffic, so these kernels are built
+// around moving each byte once.
 //
-// Forward: one workgroup (2 waves) per 64-row tile.  K and V of the tile go
-// to LDS, each wave keeps 32 query rows as the register operand, and the
-// scores of a row are complete after one tile, so the softmax is a plain one
-// (exact row max, no rescaling).  Computed transposed like the general
-// forward kernel: S^T = K Q^T, O^T = V^T P^T with bf16 MFMA 32x32x16.
+// Forward: one workgroup per tile, one wave per 32 query rows (QR = 32 or 64
+// rows of query buffer, QT of them real).  K and V of the tile go to LDS,
+// each wave keeps 32 query rows as the register operand, and the scores of a
+// row are complete after one tile, so the softmax is a plain one (exact row
+// max, no rescaling).  Computed transposed like the general forward kernel:
+// S^T = K Q^T, O^T = V^T P^T with bf16 MFMA 32x32x16.
 //
-// Backward: one workgroup (4 waves) per 64-row tile, Q, K, V and dO staged in
-// LDS once.  The dK/dV pass and the dQ pass ("IHA-CUDA", Repository
-// Structure: separate backward kernels, no atomic accumulation here) run side
-// by side on different waves of the same workgroup: waves 0-1 own 32 keys
-// each (dV^T += dO^T P, dK^T += Q^T dS), waves 2-3 own 32 queries each
-// (dQ^T += K^T dS^T).  Because the tile holds every key a query row can see,
-// the row sums D_i = sum_j P_ij dP_ij (equal to sum_c dO_ic O_ic, the
+// Backward: one workgroup per tile, Q, K, V and dO staged in LDS once.  The
+// dK/dV pass and the dQ pass ("IHA-CUDA", Repository Structure: separate
+// backward kernels, no atomic accumulation here) run side by side on
+// different waves of the same workgroup: waves 0-1 own 32 keys each
+// (dV^T += dO^T P, dK^T += Q^T dS), the waves after them own 32 query rows
+// each (dQ^T += K^T dS^T).  Because the tile holds every key a query row can
+// see, the row sums D_i = sum_j P_ij dP_ij (equal to sum_c dO_ic O_ic, the
 // "dPsum" of the backward pre-pass) are taken by the dQ waves from their own
 // P and dP and handed to the dK/dV waves through LDS: O is never read and the
 // backward makes one pass over HBM.
@@ -29,37 +34,56 @@ namespace attn {
 
 namespace {
 
-constexpr int kTile = 64;
+constexpr int kTile = 64;  // keys per tile
 
-// visibility inside a tile: rows and keys share a window (window = 1 << wshift
-// divides 64, so windows never cross tiles); a row >= n sees nothing and
-// every key of a row < n's window is < n (n is a multiple of the window).
-__device__ __forceinline__ bool local_vis(int qi, int kj, int n, int wshift) {
-  return qi < n && (qi >> wshift) == (kj >> wshift);
+// Tile geometry: key window w = 1 << lw, query rows per window wq = 1 << lq;
+// tile t holds keys [64 t, 64 t + 64) and query rows [QT t, QT t + QT) with
+// QT = (64 >> lw) << lq.  Query row r and key c of a tile (both counted from
+// the tile's start, which is window-aligned on both sides) see each other iff
+// row r is real and r >> lq == c >> lw.  A real row's window keys all exist
+// (Nk is a multiple of w), so keys past Nk are never visible.
+struct LocalTile {
+  int lw, lq, qt;  // log2 w, log2 wq, query rows per tile
+  int tq0, qend;   // first query row of the tile, end of its real rows
+  __device__ __forceinline__ bool real(int r) const { return tq0 + r < qend; }  // implies r < qt
+  __device__ __forceinline__ bool vis(int r, int c) const { return real(r) && (r >> lq) == (c >> lw); }
+};
+
+__device__ __forceinline__ LocalTile local_tile(int tile, int nq, int lw, int lq) {
+  LocalTile t;
+  t.lw = lw;
+  t.lq = lq;
+  t.qt = (kTile >> lw) << lq;
+  t.tq0 = tile * t.qt;
+  t.qend = min(nq, t.tq0 + t.qt);
+  return t;
 }
 
 // ------------------------------------------------------------------ forward
 
-template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int wshift) {
-  constexpr int NT = 128, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
+// QR: query buffer rows (32 when QT <= 32, else 64); one wave per 32 rows
+template <int D, int QR>
+__global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
+  constexpr int NT = 2 * QR, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[TE];
 
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);
   const int bh = blockIdx.x / ntile;
-  const int t0 = (blockIdx.x % ntile) * kTile;
-  const int n = a.nq;
+  const int tile = blockIdx.x % ntile;
+  const int tk0 = tile * kTile;
+  const LocalTile lt = local_tile(tile, a.nq, lw, lq);
 
-  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * n * D;
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * n * D;
-  const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * n * D;
+  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * a.nq * D;
+  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
+  const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * a.nk * D;
 
-  dma_tile<kTile, D, NT>(sK, K, t0, n, tid);
-  dma_tile<kTile, D, NT>(sV, V, t0, n, tid);
-  const int myq = t0 + wave * 32 + (lane & 31);
-  const bool qvalid = myq < n;
+  dma_tile<kTile, D, NT>(sK, K, tk0, a.nk, tid);
+  dma_tile<kTile, D, NT>(sV, V, tk0, a.nk, tid);
+  const int myr = wave * 32 + (lane & 31);  // this lane's query row in the tile
+  const int myq = lt.tq0 + myr;
+  const bool qvalid = lt.real(myr);
   bf16x8 qop[KC];
   load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
   __syncthreads();
@@ -72,7 +96,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void f
     for (int kc = 0; kc < KC; ++kc)
       s[mb] = mfma32(lds_row8<D>(sK, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
   }
-  const bool full = wshift == 6 && t0 + kTile <= n;
+  // one 64-key window of 64 rows, whole: nothing to mask
+  const bool full = lw == 6 && lq == 6 && tk0 + kTile <= a.nk;
   const float sl2 = a.scale * kLog2e;
   float mx = -INFINITY;
 #pragma unroll
@@ -81,8 +106,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void f
     for (int e = 0; e < 16; ++e) {
       float x = s[mb][e] * sl2;
       if (!full) {
-        const int key = t0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
-        if (!local_vis(myq, key, n, wshift)) x = -INFINITY;
+        const int key = 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+        if (!lt.vis(myr, key)) x = -INFINITY;
       }
       s[mb][e] = x;
       mx = fmaxf(mx, x);
@@ -113,48 +138,51 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void f
   // O rows through LDS (sK is free once every wave is past its products) so
   // that the global stores are whole rows, 16 bytes per lane
   __syncthreads();
-  acc_to_lds<D>(sK, wave * 32 + (lane & 31), oacc, qvalid ? 1.f / l : 0.f, gq);
-  if (qvalid && gq == 0) a.lse[(int64_t)bh * n + myq] = (mb2 + log2f(l)) * kLn2;
+  acc_to_lds<D>(sK, myr, oacc, qvalid ? 1.f / l : 0.f, gq);
+  if (qvalid && gq == 0) a.lse[(int64_t)bh * a.nq + myq] = (mb2 + log2f(l)) * kLn2;
   __syncthreads();
-  store_tile<kTile, D, NT>((uint16_t*)a.o + (int64_t)bh * n * D, t0, n, sK, tid);
+  store_tile<QR, D, NT>((uint16_t*)a.o + (int64_t)bh * a.nq * D, lt.tq0, lt.qend, sK, tid);
 }
 
 // ----------------------------------------------------------------- backward
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, int wshift) {
-  constexpr int NT = 256, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[TE];  // dO
-  __shared__ __attribute__((aligned(16))) float sL[kTile];           // lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[kTile];           // D_i
+// QR: query buffer rows; waves 0-1 own the tile's keys, the QR / 32 waves
+// after them its query rows
+template <int D, int QR>
+__global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int ntile, int lw, int lq) {
+  constexpr int NT = 128 + 2 * QR, KE = tile_elems<kTile, D>(), QE = tile_elems<QR, D>();
+  constexpr int KC = D / 16, DB = D / 32, QB = QR / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[QE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[KE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[KE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[QE];  // dO
+  __shared__ __attribute__((aligned(16))) float sL[QR];     // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[QR];     // D_i
 
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);
   const int bh = blockIdx.x / ntile;
-  const int t0 = (blockIdx.x % ntile) * kTile;
-  const int n = a.nq;
-  const int64_t base = (int64_t)bh * n * D;
+  const int tile = blockIdx.x % ntile;
+  const int tk0 = tile * kTile;
+  const LocalTile lt = local_tile(tile, a.nq, lw, lq);
+  const int64_t qbase = (int64_t)bh * a.nq * D, kbase = (int64_t)bh * a.nk * D;
 
-  dma_tile<kTile, D, NT>(sQ, (const uint16_t*)a.q + base, t0, n, tid);
-  dma_tile<kTile, D, NT>(sK, (const uint16_t*)a.k + base, t0, n, tid);
-  dma_tile<kTile, D, NT>(sV, (const uint16_t*)a.v + base, t0, n, tid);
-  dma_tile<kTile, D, NT>(sG, (const uint16_t*)a.dout + base, t0, n, tid);
-  if (tid < kTile) {
-    const int r = t0 + tid;
-    sL[tid] = r < n ? a.lse[(int64_t)bh * n + r] * kLog2e : 0.f;
-  }
+  dma_tile<QR, D, NT>(sQ, (const uint16_t*)a.q + qbase, lt.tq0, lt.qend, tid);
+  dma_tile<kTile, D, NT>(sK, (const uint16_t*)a.k + kbase, tk0, a.nk, tid);
+  dma_tile<kTile, D, NT>(sV, (const uint16_t*)a.v + kbase, tk0, a.nk, tid);
+  dma_tile<QR, D, NT>(sG, (const uint16_t*)a.dout + qbase, lt.tq0, lt.qend, tid);
+  if (tid < QR) sL[tid] = lt.real(tid) ? a.lse[(int64_t)bh * a.nq + lt.tq0 + tid] * kLog2e : 0.f;
   __syncthreads();
 
   const float sl2 = a.scale * kLog2e;
-  const bool full = wshift == 6 && t0 + kTile <= n;
+  const bool full = lw == 6 && lq == 6 && tk0 + kTile <= a.nk;
   const bool dq_wave = wave >= 2;
-  const int own = 32 * (wave & 1) + (lane & 31);  // this lane's key (dK/dV) or query (dQ) in the tile
+  // this lane's key (dK/dV waves) or query row (dQ waves) in the tile
+  const int own = 32 * (dq_wave ? wave - 2 : wave) + (lane & 31);
 
   // dK/dV waves: x[qt] = P, y[qt] = dP for query rows 32 qt + ..., lane = key.
   // dQ waves:    x[mb] = P^T, y[mb] = dP^T for keys 32 mb + ..., lane = query.
+  static_assert(QB <= 2, "at most 64 query rows per tile");
   f32x16 x[2], y[2];
   f32x16 acc0[DB], acc1[DB];  // dK^T, dV^T (dK/dV waves) or dQ^T (dQ waves, acc0)
 #pragma unroll
@@ -164,7 +192,6 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
   }
 
   if (dq_wave) {
-    const int qi = t0 + own;
     const float lse2 = sL[own];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -183,8 +210,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = t0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
-        const bool vis = full || local_vis(qi, key, n, wshift);
+        const int key = 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+        const bool vis = full || lt.vis(own, key);
         const float p = vis ? fast_exp2(fmaf(x[mb][e], sl2, -lse2)) : 0.f;
         x[mb][e] = p;
         dsum = fmaf(p, y[mb][e], dsum);
@@ -196,9 +223,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[mb][e] = x[mb][e] * (y[mb][e] - dsum);
   } else {
-    const int kj = t0 + own;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QB; ++qt) {
       x[qt] = f32x16{};
       y[qt] = f32x16{};
 #pragma unroll
@@ -214,8 +240,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * i + j;
-          const int qi = t0 + 32 * qt + 8 * i + 4 * gq + j;
-          const bool vis = full || local_vis(qi, kj, n, wshift);
+          const bool vis = full || lt.vis(32 * qt + 8 * i + 4 * gq + j, own);
           x[qt][e] = vis ? fast_exp2(fmaf(x[qt][e], sl2, -L4[j])) : 0.f;
         }
       }
@@ -243,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
     }
   } else {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QB; ++qt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[32 * qt + 8 * i + 4 * gq]);
@@ -267,30 +292,51 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs a, int ntile, in
     acc_to_lds<D>(sV, own, acc1, 1.f, gq);
   }
   __syncthreads();
-  store_tile<kTile, D, NT>((uint16_t*)a.dq + base, t0, n, sQ, tid);
-  store_tile<kTile, D, NT>((uint16_t*)a.dk + base, t0, n, sK, tid);
-  store_tile<kTile, D, NT>((uint16_t*)a.dv + base, t0, n, sV, tid);
+  store_tile<QR, D, NT>((uint16_t*)a.dq + qbase, lt.tq0, lt.qend, sQ, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.dk + kbase, tk0, a.nk, sK, tid);
+  store_tile<kTile, D, NT>((uint16_t*)a.dv + kbase, tk0, a.nk, sV, tid);
 }
 
-int shift_of(int w) {
+int log2_of(int w) {
   int s = 0;
   while ((1 << s) < w) ++s;
   return s;
 }
 
+// the tile geometry of a launch: log2 of both windows, tiles per (b, h)
+struct LocalLaunch {
+  int lw, lq, ntile;
+  bool wide;  // more than 32 query rows per tile
+};
+
+LocalLaunch local_launch(const MaskGeom& g) {
+  LocalLaunch l;
+  l.lw = log2_of(g.window);
+  l.lq = log2_of(g.window_q);
+  l.ntile = (g.nk + kTile - 1) / kTile;
+  l.wide = ((kTile >> l.lw) << l.lq) > 32;
+  return l;
+}
+
 template <int D>
 int fwd_d(const FwdArgs& a, hipStream_t s) {
-  const int ntile = (a.nq + kTile - 1) / kTile;
-  hipLaunchKernelGGL((fwd_local_kernel<D>), dim3((unsigned)((int64_t)ntile * a.B * a.H)),
-                     dim3(128), 0, s, a, ntile, shift_of(a.mg.window));
+  const LocalLaunch l = local_launch(a.mg);
+  const dim3 grid((unsigned)((int64_t)l.ntile * a.B * a.H));
+  if (l.wide)
+    hipLaunchKernelGGL((fwd_local_kernel<D, 64>), grid, dim3(128), 0, s, a, l.ntile, l.lw, l.lq);
+  else
+    hipLaunchKernelGGL((fwd_local_kernel<D, 32>), grid, dim3(64), 0, s, a, l.ntile, l.lw, l.lq);
   return (int)hipGetLastError();
 }
 
 template <int D>
 int bwd_d(const BwdArgs& a, hipStream_t s) {
-  const int ntile = (a.nq + kTile - 1) / kTile;
-  hipLaunchKernelGGL((bwd_local_kernel<D>), dim3((unsigned)((int64_t)ntile * a.B * a.H)),
-                     dim3(256), 0, s, a, ntile, shift_of(a.mg.window));
+  const LocalLaunch l = local_launch(a.mg);
+  const dim3 grid((unsigned)((int64_t)l.ntile * a.B * a.H));
+  if (l.wide)
+    hipLaunchKernelGGL((bwd_local_kernel<D, 64>), grid, dim3(256), 0, s, a, l.ntile, l.lw, l.lq);
+  else
+    hipLaunchKernelGGL((bwd_local_kernel<D, 32>), grid, dim3(192), 0, s, a, l.ntile, l.lw, l.lq);
   return (int)hipGetLastError();
 }
 

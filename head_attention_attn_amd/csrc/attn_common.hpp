@@ -9,9 +9,11 @@
 //   causal  [0, min(i + 1, Nk))
 //   sliding [max(0, i - W + 1), min(i + 1, Nk))     W keys incl. the diagonal
 //                                                   ("IHA-CUDA", FLOP Matching)
-//   block   [floor(i/W)*W, min(floor(i/W)*W + W, Nk))   independent windows
-//                                                   ("hiera-optim" sdist,
-//                                                   MaskUnitAttentionFast)
+//   block   [floor(i/Wq)*W, floor(i/Wq)*W + W)          independent windows
+//                                                   of W keys and Wq query
+//                                                   rows ("hiera-optim" sdist,
+//                                                   MaskUnitAttentionFast;
+//                                                   Wq < W with pooled queries)
 // and, equivalently, an interval of queries per key j:
 //     col_lo(j) <= i < col_hi(j).
 // Both bounds are non-decreasing in i (resp. j), so the keys a block of rows
@@ -39,7 +41,8 @@ constexpr int kAnyMask = -1;
 struct MaskGeom {
   int mode;
   int nq, nk;
-  int window;  // W for sliding / block; unused otherwise
+  int window;    // W for sliding, the key window length for block; unused otherwise
+  int window_q;  // block: query rows per window (= window unless queries are pooled)
 
   ATTN_HD int imin(int a, int b) const { return a < b ? a : b; }
   ATTN_HD int imax(int a, int b) const { return a > b ? a : b; }
@@ -47,25 +50,25 @@ struct MaskGeom {
   // keys visible to query row i: [row_lo(i), row_hi(i))
   ATTN_HD int row_lo(int i) const {
     if (mode == kSliding) return imax(0, i - window + 1);
-    if (mode == kBlock) return (i / window) * window;
+    if (mode == kBlock) return (i / window_q) * window;
     return 0;
   }
   ATTN_HD int row_hi(int i) const {
     if (mode == kCausal || mode == kSliding) return imin(i + 1, nk);
-    if (mode == kBlock) return imin((i / window) * window + window, nk);
+    if (mode == kBlock) return imin((i / window_q) * window + window, nk);
     return nk;
   }
   // queries that see key j: [col_lo(j), col_hi(j))
   ATTN_HD int col_lo(int j) const {
     if (j >= nk) return nq;
     if (mode == kCausal || mode == kSliding) return imin(j, nq);
-    if (mode == kBlock) return imin((j / window) * window, nq);
+    if (mode == kBlock) return imin((j / window) * window_q, nq);
     return 0;
   }
   ATTN_HD int col_hi(int j) const {
     if (j >= nk) return nq;
     if (mode == kSliding) return imin(j + window, nq);
-    if (mode == kBlock) return imin((j / window) * window + window, nq);
+    if (mode == kBlock) return imin((j / window) * window_q + window_q, nq);
     return nq;
   }
   // keys visible to any row of [a, b) (b > a): [lo, hi), possibly empty
@@ -79,9 +82,14 @@ struct MaskGeom {
     *hi = col_hi(imin(b, nk) - 1);
     if (a >= nk) *hi = *lo;
   }
-  // every query row sees only keys of its own 64-row tile (block-local with a
-  // window dividing 64; Nq == Nk is guaranteed for block-local)
-  ATTN_HD bool local64() const { return mode == kBlock && window >= 1 && 64 % window == 0; }
+  // every query row sees only keys of its own 64-key tile: block-local with a
+  // key window dividing 64 and a query window dividing the key window (both
+  // then powers of two); tile t holds keys [64 t, 64 t + 64) and query rows
+  // [QT t, QT t + QT), QT = 64 / window * window_q
+  ATTN_HD bool local64() const {
+    return mode == kBlock && window >= 1 && 64 % window == 0 && window_q >= 1 &&
+           window % window_q == 0;
+  }
   // every (row, key) of rows [a, b) x keys [j0, j1) visible; needs b <= nq, j1 <= nk
   ATTN_HD bool tile_full(int a, int b, int j0, int j1) const {
     if (b > nq || j1 > nk) return false;

@@ -16,6 +16,14 @@ are synthetic i.i.d. N(0, 1)):
   windows of 64 contiguous tokens, batch 128 ("hiera-optim 0.1.0", Results:
   Hiera-Base 224x224, B=128; sdist mask_unit.py: windows as independent
   batches).
+* block_pooled_hiera -- the mask-unit block where Hiera pools its queries
+  (hiera-optim sdist mask_unit.py, ``MaskUnitAttentionFast.forward`` with
+  ``q_stride`` = 4; the module docstring names the pooled stage's T = 16):
+  the 3136 keys of the 56x56 grid in 49 windows of 64, each window holding
+  64 / 4 = 16 max-pooled query rows, so Nq = 784.  The stage's width doubles
+  (hierarchical encoders: embed_dim * 2^stage) and so do its heads, leaving
+  head_dim = 96: B=128, H=2, d=96.  Windows are contiguous runs here (the
+  permute that makes them contiguous is the caller's).
 * global_vision -- Hiera's global-attention stage on a 14x14 grid.
 * causal_lm -- causal attention of a 20-head, d=128 LLaMA at N=8192
   ("IHA-CUDA", End-to-End Training Benchmark).
@@ -56,6 +64,7 @@ WORKLOADS = {
     for w in (
         Workload("tiny_exact_fp32", 1, 2, 128, 128, 64, "fp32", "none"),
         Workload("block_local_hiera", 128, 1, 3136, 3136, 96, "bf16", "block", 64),
+        Workload("block_pooled_hiera", 128, 2, 784, 3136, 96, "bf16", "block", 64),
         Workload("global_vision", 128, 4, 196, 196, 96, "bf16", "none"),
         Workload("causal_lm", 1, 20, 8192, 8192, 128, "bf16", "causal"),
         Workload("sliding_pseudo_head", 1, 80, 4096, 4096, 128, "bf16", "sliding", 1024),

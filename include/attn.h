@@ -39,8 +39,12 @@
  *     ATTN_MASK_NONE     every key
  *     ATTN_MASK_CAUSAL   j <= i
  *     ATTN_MASK_SLIDING  i - window < j <= i        (window >= 1)
- *     ATTN_MASK_BLOCK    i / window == j / window   (integer division; needs
- *                                                    Nq == Nk, Nk % window == 0)
+ *     ATTN_MASK_BLOCK    i / Wq == j / window       (integer division; the
+ *                        Nk / window windows of `window` keys each hold
+ *                        Wq = Nq / (Nk / window) query rows -- Wq = window when
+ *                        Nq == Nk, fewer with pooled queries as in Hiera's
+ *                        q_stride > 1 mask units; needs Nk % window == 0 and
+ *                        Nq % (Nk / window) == 0)
  * A query row that sees no key gets O = 0, lse = -inf, dQ = 0.
  *
  * Ownership: the caller allocates every buffer, including the backward
@@ -174,8 +178,10 @@ enum attn_pass {
 /*
  * attn_bwd_fused -- 1 when attn_bwd runs as ONE fused kernel for these
  * arguments, else 0 (also 0 for arguments attn_bwd would reject).  Fused:
- * bf16 block-local attention whose window divides 64, where every query row
- * sees keys of its own 64-row tile only ("hiera-optim 0.1.0" sdist,
+ * bf16 block-local attention whose window divides 64 and whose query rows per
+ * window Wq = Nq / (Nk / window) divide the window (Wq = window, or pooled
+ * queries with an integer q_stride = window / Wq), where every query row
+ * sees keys of its own 64-key tile only ("hiera-optim 0.1.0" sdist,
  * mask_unit.py: mask-unit windows as independent dense attentions).  One
  * workgroup then holds a whole tile: its dK/dV waves and its dQ waves run the
  * two backward passes side by side, the row sums D_i are formed in-tile as

@@ -7,13 +7,15 @@
 
 using attn::MaskGeom;
 
+static int g_wq = 0;  // block: query rows per window of the case being checked
+
 static bool sees(int mode, int W, int nk, int i, int j) {
   if (j < 0 || j >= nk) return false;
   switch (mode) {
     case attn::kNone: return true;
     case attn::kCausal: return j <= i;
     case attn::kSliding: return i - W < j && j <= i;
-    case attn::kBlock: return i / W == j / W;
+    case attn::kBlock: return i / g_wq == j / W;
   }
   return false;
 }
@@ -28,7 +30,8 @@ static int fails = 0;
   } while (0)
 
 static void check(int mode, int W, int nq, int nk) {
-  MaskGeom g{mode, nq, nk, W};
+  g_wq = mode == attn::kBlock ? nq / (nk / W) : 0;
+  MaskGeom g{mode, nq, nk, W, g_wq};
   for (int i = 0; i < nq; ++i)
     for (int j = 0; j < nk; ++j) {
       const bool v = sees(mode, W, nk, i, j);
@@ -37,6 +40,24 @@ static void check(int mode, int W, int nq, int nk) {
       CHECK(v == (g.col_lo(j) <= i && i < g.col_hi(j)), "col interval m%d W%d %dx%d i%d j%d\n", mode, W,
             nq, nk, i, j);
     }
+  // single-tile geometry of block-local shapes with local64(): tile t holds
+  // keys [64 t, 64 t + 64) and query rows [QT t, QT t + QT); inside a tile,
+  // row r and key c see each other iff r >> log2(Wq) == c >> log2(W)
+  if (g.local64()) {
+    int lw = 0, lq = 0;
+    while ((1 << lw) < W) ++lw;
+    while ((1 << lq) < g_wq) ++lq;
+    CHECK((1 << lw) == W && (1 << lq) == g_wq, "local64 windows not powers of two W%d Wq%d\n", W, g_wq);
+    const int qt = (64 >> lw) << lq;
+    for (int i = 0; i < nq; ++i)
+      for (int j = 0; j < nk; ++j) {
+        const bool v = sees(mode, W, nk, i, j);
+        if (v) CHECK(i / qt == j / 64, "local64 pair crosses tiles W%d %dx%d i%d j%d\n", W, nq, nk, i, j);
+        if (i / qt == j / 64)
+          CHECK(v == (((i % qt) >> lq) == ((j % 64) >> lw)), "local64 in-tile rule W%d %dx%d i%d j%d\n",
+                W, nq, nk, i, j);
+      }
+  }
   const int steps[] = {1, 3, 4, 7, 16, 32};
   for (int bs : steps) {
     for (int a = 0; a < nq; a += bs) {
@@ -88,16 +109,17 @@ static void check(int mode, int W, int nq, int nk) {
 }
 
 int main() {
-  const int sizes[] = {1, 2, 5, 16, 17, 33, 64, 65};
+  const int sizes[] = {1, 2, 4, 5, 16, 17, 33, 64, 65, 96, 128};
   for (int nq : sizes)
     for (int nk : sizes) {
       check(attn::kNone, 0, nq, nk);
       check(attn::kCausal, 0, nq, nk);
       const int wins[] = {1, 2, 3, 16, 40, 100};
       for (int W : wins) check(attn::kSliding, W, nq, nk);
-      if (nq == nk)
-        for (int W = 1; W <= nk; ++W)
-          if (nk % W == 0) check(attn::kBlock, W, nq, nk);
+      // block: nk / W windows of W keys, nq / (nk / W) query rows each
+      // (nq < nk: pooled queries)
+      for (int W = 1; W <= nk; ++W)
+        if (nk % W == 0 && nq % (nk / W) == 0) check(attn::kBlock, W, nq, nk);
     }
   std::printf("%d failures\n", fails);
   return fails ? 1 : 0;

@@ -77,6 +77,7 @@ def _ds_blocks_from_visibility(mask, window, nq, nk):
     (128, 128, "causal", 0), (333, 333, "causal", 0), (200, 200, "none", 0),
     (300, 300, "sliding", 70), (256, 256, "block", 128), (150, 40, "sliding", 16),
     (37, 150, "causal", 0), (100, 37, "none", 0), (40, 150, "sliding", 16),
+    (96, 384, "block", 96), (100, 200, "block", 40),      # pooled queries
 ])
 def test_workspace_size_ds_counts_visible_blocks(lib, nq, nk, mask, window):
     """attn_bwd_workspace_size_ds = row sums + 2 KB per visible 32 x 32
@@ -85,6 +86,18 @@ def test_workspace_size_ds_counts_visible_blocks(lib, nq, nk, mask, window):
     base = lib.attn_bwd_workspace_size(B, H, nq)
     got = lib.attn_bwd_workspace_size_ds(0, B, H, nq, nk, 128, MASK[mask], window)
     assert got == base + B * H * _ds_blocks_from_visibility(mask, window, nq, nk) * 2048
+
+
+def test_pooled_block_single_tile_dispatch(lib):
+    """Key windows dividing 64 whose query windows divide them run as single
+    tiles (fused backward), pooled or not; other block shapes do not."""
+    assert lib.attn_bwd_fused(0, 1, 1, 3136, 3136, 96, 3, 64) == 1
+    assert lib.attn_bwd_fused(0, 1, 1, 784, 3136, 96, 3, 64) == 1     # 16 query rows per window
+    assert lib.attn_bwd_fused(0, 1, 1, 4, 64, 96, 3, 16) == 1         # one query row per window
+    assert lib.attn_bwd_fused(0, 1, 1, 12, 64, 96, 3, 16) == 0        # 3 rows per window of 16
+    assert lib.attn_bwd_fused(0, 1, 1, 20, 80, 96, 3, 80) == 0        # window 80 does not divide 64
+    assert lib.attn_bwd_fused(1, 1, 1, 784, 3136, 96, 3, 64) == 0     # fp32
+    assert lib.attn_bwd_fused(0, 1, 1, 15, 64, 96, 3, 16) == 0        # invalid: 4 windows, 15 rows
 
 
 def test_workspace_size_ds_where_it_does_not_apply(lib):
@@ -139,6 +152,7 @@ def test_valid_arguments_pass(lib):
         assert check_bwd(lib, mask=mask, window=window) == OK
     assert check_fwd(lib, dtype=FP32, d=96) == OK
     assert check_fwd(lib, Nq=7, Nk=300, mask=1) == OK          # Nq != Nk, top-left causal
+    assert check_fwd(lib, Nq=50, Nk=100, mask=3, window=4) == OK  # pooled: 25 windows of 2 rows x 4 keys
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -154,7 +168,8 @@ def test_valid_arguments_pass(lib):
     (dict(mask=2, window=0), INVALID),
     (dict(mask=3, window=0), INVALID),
     (dict(mask=3, window=7), INVALID),            # 100 % 7 != 0
-    (dict(mask=3, window=4, Nk=96), INVALID),     # block needs Nq == Nk
+    (dict(mask=3, window=4, Nk=96), INVALID),     # 24 windows do not divide Nq = 100
+    (dict(mask=3, window=4, Nq=24, Nk=100), INVALID),  # 25 windows do not divide Nq = 24
     (dict(scale=float("nan")), INVALID),
     (dict(scale=float("inf")), INVALID),
     (dict(q=0), INVALID),

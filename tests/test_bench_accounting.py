@@ -11,10 +11,10 @@ from oracle import visible
 @pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 1),
                                          ("sliding", 7), ("sliding", 500), ("block", 1),
                                          ("block", 8), ("block", 48)])
-@pytest.mark.parametrize("nq,nk", [(48, 48), (1, 1), (37, 100), (100, 37)])
+@pytest.mark.parametrize("nq,nk", [(48, 48), (1, 1), (37, 100), (100, 37), (12, 48), (6, 96)])
 def test_visible_pairs_match_the_oracle_mask(mask, window, nq, nk):
-    if mask == "block" and (nq != nk or nk % window):
-        pytest.skip("block-local needs Nq == Nk divisible by the window")
+    if mask == "block" and (nk % window or nq % (nk // window)):
+        pytest.skip("block-local needs Nk divisible by the window and Nq by the window count")
     assert bench.visible_pairs(mask, window, nq, nk) == int(visible(mask, window, nq, nk).sum())
 
 
@@ -23,6 +23,7 @@ def test_workload_pair_counts():
     causal triangle N(N+1)/2; the sliding band sum of min(i+1, 1024)."""
     pc = {n: bench.visible_pairs(w.mask, w.window, w.Nq, w.Nk) for n, w in WORKLOADS.items()}
     assert pc["block_local_hiera"] == 49 * 64 * 64
+    assert pc["block_pooled_hiera"] == 49 * 16 * 64
     assert pc["global_vision"] == 196 * 196
     assert pc["causal_lm"] == 8192 * 8193 // 2
     assert pc["sliding_pseudo_head"] == 1024 * 1025 // 2 + (4096 - 1024) * 1024

@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 SAMPLES = {
     "block_local_hiera": [(0, 0), (77, 0), (127, 0)],
+    "block_pooled_hiera": [(0, 0), (63, 1), (127, 1)],
     "global_vision": [(0, 0), (0, 3), (127, 2)],
     "causal_lm": [(0, 0), (0, 19)],
     "sliding_pseudo_head": [(0, 0), (0, 41), (0, 79)],

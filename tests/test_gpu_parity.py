@@ -233,6 +233,39 @@ def test_block_local_single_tile_path(d, window, n):
                 amax_rel=2.0 ** -8 if window <= 4 else 0.0)
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("nw,w,wq,single_tile", [
+    (5, 48, 12, False),   # 60 query rows over 240 keys: one partial query tile
+    (7, 40, 10, False),   # windows straddle 64-key tiles
+    (37, 6, 3, False),    # 111 queries, 222 keys: ragged tails on both sides
+    (9, 64, 16, True),    # Hiera's q_stride 4: 16 query rows per 64-key tile
+    (11, 32, 16, True),   # 32 rows per tile, partial last tile (352 keys)
+    (13, 16, 1, True),    # one pooled query per window, 4 rows per tile
+    (7, 8, 4, True),      # 56 keys: one partial tile of 28 rows
+    (5, 64, 32, True),    # q_stride 2
+    (3, 64, 64, True),    # no pooling, 64-key windows
+])
+def test_block_pooled_queries(d, nw, w, wq, single_tile):
+    """Block mask with pooled queries: Nk / w windows of w keys each hold
+    Nq / (Nk / w) = wq query rows (Hiera's q_stride = w / wq).  Key windows
+    dividing 64 with wq dividing w run as single tiles (64 keys and their
+    64 wq / w query rows), the rest on the general kernels."""
+    nq, nk = nw * wq, nw * w
+    q, k, v, _ = make_inputs(1, 1, nq, nk, d, "bf16", seed=14)
+    assert attn.binding.bwd_fused(q.cuda(), k.cuda(), v.cuda(), mask="block", window=w) == single_tile
+    parity_case(2, 2, nq, nk, d, "bf16", "block", w, seed=14)
+
+
+@pytest.mark.parametrize("keep_ds", [True, False])
+def test_block_pooled_d128_both_dq_paths(keep_ds):
+    """Pooled block mask at d = 128 with and without the kept-dS dQ pass."""
+    parity_case(2, 2, 13 * 24, 13 * 96, 128, "bf16", "block", 96, seed=15, keep_ds=keep_ds)
+
+
+def test_block_pooled_fp32():
+    parity_case(2, 2, 9 * 8, 9 * 32, 64, "fp32", "block", 32, seed=16)
+
+
 def test_fused_backward_rejects_partial_pass_sets():
     q, k, v, do = (t.cuda() for t in make_inputs(1, 1, 128, 128, 96, "bf16", seed=11))
     o, lse = attn.fwd(q, k, v, mask="block", window=64)
