@@ -10,8 +10,7 @@ backward kernels through a ``torch.autograd.Function`` wrapper, and
 ``MaskUnitAttentionFast``) is an ``nn.Module`` whose attention core takes
 q, k, v of shape [batch, heads, tokens, head_dim] and returns O of that
 shape.  Nothing here does arithmetic on the tensors: shapes are
-checked, contiguous inputs are required, and every product and softmax runs
-in the library's kernels.
+checked, and every product and softmax runs in the library's kernels.
 """
 from __future__ import annotations
 
@@ -23,9 +22,10 @@ from . import binding
 class FusedAttentionFunction(torch.autograd.Function):
     """O = softmax(scale * Q K^T + mask) V, with dQ, dK, dV from ``attn_bwd``.
 
-    Inputs: contiguous device tensors q [B, H, Nq, d], k and v [B, H, Nk, d]
-    (bf16 or fp32), the mask name, its window and the scale (None: d^-0.5).
-    Returns O [B, H, Nq, d].  ``keep_ds`` picks the backward workspace: large
+    Inputs: device tensors q [B, H, Nq, d], k and v [B, H, Nk, d] with any
+    row strides (views of a projection output need no copy), or window-split
+    [B, nw, H, T, d] views for the block mask (bf16 or fp32); the mask name,
+    its window and the scale (None: d^-0.5).  Returns O shaped like q.  ``keep_ds`` picks the backward workspace: large
     enough for the dQ pass to read dS kept by the dK/dV pass where that path
     applies (``attn_bwd_workspace_size_ds``), else the minimum."""
 
@@ -40,8 +40,11 @@ class FusedAttentionFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
         mask, window, scale, keep_ds = ctx.cfg
-        # the kernels read dO as a contiguous [B, H, Nq, d] tensor of q's dtype
-        do = do.to(q.dtype).contiguous()
+        # dO in q's dtype; the kernels take any row strides, but a broadcast
+        # (stride 0) or unaligned gradient is copied first
+        do = do.to(q.dtype)
+        if not binding.rows_usable(do):
+            do = do.contiguous()
         dq, dk, dv = binding.bwd(q, k, v, o, lse, do, mask=mask, window=window, scale=scale,
                                  keep_ds=keep_ds)
         return dq, dk, dv, None, None, None, None

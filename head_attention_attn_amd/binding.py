@@ -21,6 +21,17 @@ DTYPE_CODES = {torch.bfloat16: 0, torch.float32: 1}
 _lib = None
 
 
+class Layout(ctypes.Structure):
+    """``attn_layout``: element strides of one tensor's rows."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64),
+                ("window", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+class Layouts(ctypes.Structure):
+    """``attn_layouts``: the layouts of every tensor argument."""
+    _fields_ = [(n, Layout) for n in ("q", "k", "v", "o", "dout", "dq", "dk", "dv")]
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -65,6 +76,17 @@ def load_library():
                                    ctypes.c_int, i64, vp, vp, vp, vp, fp, vp, vp, vp, vp,
                                    vp, ctypes.c_size_t]
     lib.attn_check_bwd.restype = ctypes.c_int
+    lp = ctypes.POINTER(Layouts)
+    lib.attn_fwd_strided.argtypes = lib.attn_fwd.argtypes[:-1] + [lp, vp]
+    lib.attn_fwd_strided.restype = ctypes.c_int
+    lib.attn_bwd_strided.argtypes = [ctypes.c_int] + lib.attn_bwd.argtypes[:-1] + [lp, vp]
+    lib.attn_bwd_strided.restype = ctypes.c_int
+    lib.attn_check_fwd_strided.argtypes = lib.attn_check_fwd.argtypes + [lp]
+    lib.attn_check_fwd_strided.restype = ctypes.c_int
+    lib.attn_check_bwd_strided.argtypes = lib.attn_check_bwd.argtypes + [lp]
+    lib.attn_check_bwd_strided.restype = ctypes.c_int
+    lib.attn_layouts_contiguous.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64, lp]
+    lib.attn_layouts_contiguous.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -75,18 +97,94 @@ def status_string(status: int) -> str:
     return load_library().attn_status_string(int(status)).decode()
 
 
-def _geometry(q, k, v):
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, N, d]")
-    B, H, Nq, d = q.shape
-    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
+def _rows(t, name):
+    """(B, H, n, T, d, Layout) of a [B, H, N, d] tensor (any row strides) or
+    of a window-split [B, nw, H, T, d] one (block mask: window w, position t
+    is token w * T + t); the d values of a row must be contiguous."""
+    if t.dim() == 4:
+        B, H, n, d = t.shape
+        sb, sh, st, sd = t.stride()
+        lay, T = Layout(sb, sh, 0, st), n
+    elif t.dim() == 5:
+        B, nw, H, T, d = t.shape
+        sb, sw, sh, st, sd = t.stride()
+        lay, n = Layout(sb, sh, sw, st), nw * T
+    else:
+        raise ValueError(f"{name} must be [B, H, N, d] or [B, nw, H, T, d]")
+    if d > 1 and sd != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return B, H, n, T, d, lay
+
+
+def rows_usable(t) -> bool:
+    """Whether ``t`` can be passed as it is: contiguous rows, a 16-byte
+    aligned base, and every stride of a dimension of size > 1 a positive
+    multiple of 16 bytes (the library checks the rest)."""
+    if t.stride(-1) != 1 or t.data_ptr() % 16:
+        return False
+    per16 = 16 // t.element_size()
+    return all(st > 0 and st % per16 == 0 for n, st in zip(t.shape[:-1], t.stride()[:-1]) if n > 1)
+
+
+def _geometry(q, k, v, mask=None, window=None):
+    """Shapes, mask and window of a call: (B, H, Nq, Nk, d, mask, window).
+    Window-split (5-D) tensors mean the block mask with window = T of k."""
+    if not (q.dim() == k.dim() == v.dim()):
+        raise ValueError("q, k, v must all be 4-D or all 5-D")
+    Bq, Hq, Nq, Tq, d, _ = _rows(q, "q")
+    B, H, Nk, Tk, dk, _ = _rows(k, "k")
+    if (Bq, Hq, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype bfloat16 or float32")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("tensors must be contiguous device tensors")
-    return B, H, Nq, k.shape[2], d
+    if q.dim() == 5:
+        if q.shape[1] != k.shape[1]:
+            raise ValueError("q and k must have the same number of windows")
+        if mask not in (None, "block") or window not in (None, 0, Tk):
+            raise ValueError("window-split tensors take the block mask with window = T of k")
+        mask, window = "block", Tk
+    return B, H, Nq, Nk, d, mask or "none", int(window or 0)
+
+
+def _is_plain(*ts):
+    return all(t.dim() == 4 and t.is_contiguous() for t in ts)
+
+
+def _empty_rows(like):
+    """An output shaped like ``like``: contiguous for 4-D; for 5-D
+    [B, nw, H, T, d], stored in token order (B, T, nw, H, d) -- position-major
+    with the window index fastest, the order Hiera's output projection reads."""
+    if like.dim() == 4:
+        return torch.empty(like.shape, dtype=like.dtype, device=like.device)
+    B, nw, H, T, d = like.shape
+    return torch.empty((B, T, nw, H, d), dtype=like.dtype, device=like.device).permute(0, 2, 3, 1, 4)
+
+
+_Q_SIDE = ("q", "o", "dout", "dq")
+
+
+def _layouts(Nq, Nk, mask, window, **ts):
+    """attn_layouts of the named tensors.  A [B, H, N, d] tensor's windows
+    (block mask) follow each other at its token stride."""
+    L = Layouts()
+    for name, t in ts.items():
+        lay = _rows(t, name)[5]
+        if t.dim() == 4:
+            n = Nq if name in _Q_SIDE else Nk
+            T = n if mask != "block" else (window if name not in _Q_SIDE else Nq // (Nk // window))
+            lay.window = T * lay.token
+        setattr(L, name, lay)
+    return L
+
+
+def _mask_args(q, mask, window):
+    """The caller's mask and window as _geometry takes them: for window-split
+    tensors the defaults ("none", 0) mean "from the tensors"."""
+    if q.dim() == 5:
+        return (None if mask == "none" else mask), (None if not window else window)
+    return mask, window
 
 
 def _scale(scale, d):
@@ -98,15 +196,23 @@ def _stream(t):
 
 
 def fwd(q, k, v, mask: str = "none", window: int = 0, scale=None, out=None, lse=None):
-    """O, lse = attention(q, k, v).  Returns (o [B,H,Nq,d] in q.dtype,
-    lse [B,H,Nq] float32)."""
+    """O, lse = attention(q, k, v).  q, k, v: [B, H, N, d] with any row
+    strides (contiguous ones take ``attn_fwd``, others ``attn_fwd_strided``),
+    or window-split [B, nw, H, T, d] views (block mask, window T).  Returns
+    (o shaped like q, in q.dtype; lse [B, H, Nq] float32)."""
     lib = load_library()
-    B, H, Nq, Nk, d = _geometry(q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    B, H, Nq, Nk, d, mask, window = _geometry(q, k, v, *_mask_args(q, mask, window))
+    o = _empty_rows(q) if out is None else out
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("out must be shaped like q")
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = lib.attn_fwd(DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d),
-                      MASK_CODES[mask], int(window), q.data_ptr(), k.data_ptr(),
-                      v.data_ptr(), o.data_ptr(), lse.data_ptr(), _stream(q))
+    args = (DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d), MASK_CODES[mask], window,
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    if _is_plain(q, k, v, o):
+        st = lib.attn_fwd(*args, _stream(q))
+    else:
+        L = _layouts(Nq, Nk, mask, window, q=q, k=k, v=v, o=o)
+        st = lib.attn_fwd_strided(*args, ctypes.byref(L), _stream(q))
     if st != 0:
         raise AttnError(st, "attn_fwd")
     return o, lse
@@ -115,9 +221,9 @@ def fwd(q, k, v, mask: str = "none", window: int = 0, scale=None, out=None, lse=
 def bwd_fused(q, k, v, mask: str = "none", window: int = 0) -> bool:
     """True when ``bwd`` runs as one fused kernel for these tensors (then
     ``passes`` must be PASS_ALL)."""
-    B, H, Nq, Nk, d = _geometry(q, k, v)
+    B, H, Nq, Nk, d, mask, window = _geometry(q, k, v, *_mask_args(q, mask, window))
     return load_library().attn_bwd_fused(DTYPE_CODES[q.dtype], B, H, Nq, Nk, d,
-                                         MASK_CODES[mask], int(window)) == 1
+                                         MASK_CODES[mask], window) == 1
 
 
 def workspace_bytes(B: int, H: int, Nq: int) -> int:
@@ -129,9 +235,9 @@ def workspace_bytes_ds(q, k, mask: str = "none", window: int = 0) -> int:
     """Backward workspace with which the dQ pass reads dS kept by the dK/dV
     pass (``attn_bwd_workspace_size_ds``); equals ``workspace_bytes`` where
     that path does not apply."""
-    B, H, Nq, d = q.shape
+    B, H, Nq, Nk, d, mask, window = _geometry(q, k, k, *_mask_args(q, mask, window))
     return int(load_library().attn_bwd_workspace_size_ds(
-        DTYPE_CODES[q.dtype], B, H, Nq, k.shape[2], d, MASK_CODES[mask], int(window)))
+        DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, MASK_CODES[mask], window))
 
 
 PASS_ROWSUM, PASS_DKDV, PASS_DQ, PASS_ALL = 1, 2, 4, 7
@@ -140,26 +246,32 @@ PASS_ROWSUM, PASS_DKDV, PASS_DQ, PASS_ALL = 1, 2, 4, 7
 def bwd(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
         workspace=None, dq=None, dk=None, dv=None, passes: int = PASS_ALL,
         keep_ds: bool = True):
-    """dQ, dK, dV of attention given dO.  Returns tensors shaped like q, k, v.
+    """dQ, dK, dV of attention given dO.  Returns tensors shaped like q, k, v
+    (any row strides, or window-split views, as for ``fwd``).
     ``passes`` (a set of PASS_* bits) restricts the call to some of the
     backward passes (``attn_bwd_passes``); the default runs all three.  When
     no workspace is given one is allocated: with ``keep_ds`` large enough
     for the dQ pass to read dS kept by the dK/dV pass, else the minimum."""
     lib = load_library()
-    B, H, Nq, Nk, d = _geometry(q, k, v)
-    if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, Nq):
+    B, H, Nq, Nk, d, mask, window = _geometry(q, k, v, *_mask_args(q, mask, window))
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape) \
+            or tuple(lse.shape) != (B, H, Nq):
         raise ValueError("o/do must match q and lse must be [B, H, Nq]")
     ws_need = workspace_bytes_ds(q, k, mask, window) if keep_ds else workspace_bytes(B, H, Nq)
     if workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    st = lib.attn_bwd_passes(int(passes), DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d),
-                      MASK_CODES[mask], int(window), q.data_ptr(), k.data_ptr(),
-                      v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                      workspace.numel() * workspace.element_size(), _stream(q))
+    dq = _empty_rows(q) if dq is None else dq
+    dk = _empty_rows(k) if dk is None else dk
+    dv = _empty_rows(v) if dv is None else dv
+    args = (int(passes), DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d),
+            MASK_CODES[mask], window, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    if _is_plain(q, k, v, o, do, dq, dk, dv):
+        st = lib.attn_bwd_passes(*args, _stream(q))
+    else:
+        L = _layouts(Nq, Nk, mask, window, q=q, k=k, v=v, o=o, dout=do, dq=dq, dk=dk, dv=dv)
+        st = lib.attn_bwd_strided(*args, ctypes.byref(L), _stream(q))
     if st != 0:
         raise AttnError(st, "attn_bwd_passes")
     return dq, dk, dv

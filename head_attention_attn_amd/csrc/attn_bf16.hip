@@ -35,7 +35,7 @@ namespace {
 
 // ------------------------------------------------------------------ forward
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, bool SR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdArgs a, int nqt) {
   static_assert(NW == 4, "O staging assumes 4 waves (two 64-row tiles)");
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, TE = tile_elems<BN, D>();
@@ -56,9 +56,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
   const int i0 = qt * BM, i1 = min(i0 + BM, a.nq);
 
-  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * a.nq * D;
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
-  const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * a.nk * D;
+  const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
+  const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
+  const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
 
   const int wa = i0 + wave * 32, wb = min(wa + 32, a.nq);
   const int myq = wa + (lane & 31);
@@ -73,11 +73,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int t0 = (lo / BN) * BN;
 
   if (lo < hi) {
-    dma_tile<BN, D, NT>(sK0, K, t0, a.nk, tid);
-    dma_tile<BN, D, NT>(sV0, V, t0, a.nk, tid);
+    dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
+    dma_tile<BN, D, NT, SR>(sV0, V, a.rv, t0, a.nk, tid);
   }
   bf16x8 qop[KC];
-  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
+  load_operand_rows<D>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
 
   float m = -INFINITY, l = 0.f;
   f32x16 oacc[DB];
@@ -140,15 +140,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __syncthreads();
     for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
       if (j0 + BN < hi) {
-        dma_tile<BN, D, NT>(sK1, K, j0 + BN, a.nk, tid);
-        dma_tile<BN, D, NT>(sV1, V, j0 + BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sV1, V, a.rv, j0 + BN, a.nk, tid);
       }
       tile(sK0, sV0, j0);
       __syncthreads();
       if (j0 + BN >= hi) break;
       if (j0 + 2 * BN < hi) {
-        dma_tile<BN, D, NT>(sK0, K, j0 + 2 * BN, a.nk, tid);
-        dma_tile<BN, D, NT>(sV0, V, j0 + 2 * BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sV0, V, a.rv, j0 + 2 * BN, a.nk, tid);
       }
       tile(sK1, sV1, j0 + BN);
       __syncthreads();
@@ -162,23 +162,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (qvalid && gq == 0)
     a.lse[(int64_t)bh * a.nq + myq] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
   __syncthreads();
-  uint16_t* O = (uint16_t*)a.o + (int64_t)bh * a.nq * D;
-  store_tile<64, D, NT>(O, i0, a.nq, sK0, tid);
-  store_tile<64, D, NT>(O, i0 + 64, a.nq, sV0, tid);
+  uint16_t* O = (uint16_t*)a.o + rslice<SR, D>(a.ro, bh, a.H, a.nq);
+  store_tile<64, D, NT, SR>(O, a.ro, i0, a.nq, sK0, tid);
+  store_tile<64, D, NT, SR>(O, a.ro, i0 + 64, a.nq, sV0, tid);
 }
 
 // ------------------------------------------------------- backward: row sums
 
-template <int D>
-__global__ __launch_bounds__(256) void dsum_bf16_kernel(const uint16_t* __restrict__ o,
-                                                        const uint16_t* __restrict__ dout,
-                                                        float* __restrict__ dsum, int64_t rows) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+// 16 rows of one (b, h) slice per workgroup, 16 lanes per row
+template <int D, bool SR>
+__global__ __launch_bounds__(256) void dsum_bf16_kernel(BwdArgs a, int nblk) {
+  const int bh = blockIdx.x / nblk;
+  const int row = (blockIdx.x % nblk) * 16 + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
   float acc = 0.f;
-  if (row < rows && li < D / 8) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + row * D + 8 * li);
-    const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + row * D + 8 * li);
+  if (row < a.nq && li < D / 8) {
+    const uint16_t* o =
+        (const uint16_t*)a.o + rslice<SR, D>(a.ro, bh, a.H, a.nq) + rrow<SR, D>(a.ro, row);
+    const uint16_t* g =
+        (const uint16_t*)a.dout + rslice<SR, D>(a.rdo, bh, a.H, a.nq) + rrow<SR, D>(a.rdo, row);
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + 8 * li);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(g + 8 * li);
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc += (float)x[s] * (float)y[s];
   }
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) void dsum_bf16_kernel(const uint16_t* __restri
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
-  if (row < rows && li == 0) dsum[row] = acc;
+  if (row < a.nq && li == 0) a.dsum[(int64_t)bh * a.nq + row] = acc;
 }
 
 // ------------------------------------------------------- backward: dK / dV
@@ -204,7 +208,7 @@ struct DkdvShape {
   static constexpr int WPE = D == 128 ? 1 : 2;
 };
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, bool SR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvShape<D>::WPE))) void dkdv_bf16_kernel(BwdArgs a, int nkt) {
   static_assert(NW == 4, "dK/dV staging assumes 4 waves");
   constexpr int KB = DkdvShape<D>::KB, BQ = DkdvShape<D>::BQ;
@@ -229,10 +233,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
   const int k0 = kt * BK, k1 = min(k0 + BK, a.nk);
 
-  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * a.nq * D;
-  const uint16_t* dO = (const uint16_t*)a.dout + (int64_t)bh * a.nq * D;
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
-  const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * a.nk * D;
+  const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
+  const uint16_t* dO = (const uint16_t*)a.dout + rslice<SR, D>(a.rdo, bh, a.H, a.nq);
+  const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
+  const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
   const float* LSE = a.lse + (int64_t)bh * a.nq;
   const float* DS = a.dsum + (int64_t)bh * a.nq;
 
@@ -246,8 +250,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   const int t0 = (lo / BQ) * BQ;
 
   auto load = [&](uint16_t* q_l, uint16_t* g_l, float* s_l, int r0) {
-    dma_tile<BQ, D, NT>(q_l, Q, r0, a.nq, tid);
-    dma_tile<BQ, D, NT>(g_l, dO, r0, a.nq, tid);
+    dma_tile<BQ, D, NT, SR>(q_l, Q, a.rq, r0, a.nq, tid);
+    dma_tile<BQ, D, NT, SR>(g_l, dO, a.rdo, r0, a.nq, tid);
     if (wave < NH) dma_rows_f32x2(s_l + 64 * wave, LSE, DS, r0 + 32 * wave, a.nq, lane);
   };
   if (lo < hi) load(sQ0, sG0, sS0, t0);
@@ -258,8 +262,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   for (int kb = 0; kb < KB; ++kb) {
     const int myk = wk0 + 32 * kb + (lane & 31);
     const bool kvalid = myk < a.nk;
-    load_operand_rows<D>(kop[kb], K + (int64_t)myk * D, kvalid, gq);
-    load_operand_rows<D>(vop[kb], V + (int64_t)myk * D, kvalid, gq);
+    load_operand_rows<D>(kop[kb], K + rrow<SR, D>(a.rk, myk), kvalid, gq);
+    load_operand_rows<D>(vop[kb], V + rrow<SR, D>(a.rv, myk), kvalid, gq);
     clo[kb] = kvalid ? mg.col_lo(myk) : 0;
     chi[kb] = kvalid ? mg.col_hi(myk) : 0;
   }
@@ -354,8 +358,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   // for whole-row 16-byte stores
   static_assert(KB * 32 * NW == 4 * BQ || KB * 32 * NW * 2 == 4 * BQ, "staging shape");
   auto bufs = [&](int i) { return i == 0 ? sQ0 : i == 1 ? sG0 : i == 2 ? sQ1 : sG1; };
-  uint16_t* dK = (uint16_t*)a.dk + (int64_t)bh * a.nk * D;
-  uint16_t* dV = (uint16_t*)a.dv + (int64_t)bh * a.nk * D;
+  uint16_t* dK = (uint16_t*)a.dk + rslice<SR, D>(a.rdk, bh, a.H, a.nk);
+  uint16_t* dV = (uint16_t*)a.dv + rslice<SR, D>(a.rdv, bh, a.H, a.nk);
   constexpr int WR = 32 * KB;                       // rows per wave
   constexpr int WPB = BQ / WR;                      // waves per buffer
 #pragma unroll
@@ -368,8 +372,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
                     pass ? 1.f : a.scale, gq);
     __syncthreads();
     uint16_t* dst = pass ? dV : dK;
+    const RowMap& rdst = pass ? a.rdv : a.rdk;
 #pragma unroll
-    for (int b = 0; b < NW / WPB; ++b) store_tile<BQ, D, NT>(dst, k0 + b * BQ, a.nk, bufs(b), tid);
+    for (int b = 0; b < NW / WPB; ++b) store_tile<BQ, D, NT, SR>(dst, rdst, k0 + b * BQ, a.nk, bufs(b), tid);
   }
 }
 
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
 // a score wave's softmax arithmetic overlaps its partner's MFMAs.  Q / dO
 // tiles cycle through three named buffers (one being loaded, one read by the
 // score waves, one by the accumulate waves), P / dS through three more.
-template <int D, int MODE>
+template <int D, int MODE, bool SR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void dkdv_pp_kernel(BwdArgs a, int nkt) {
   constexpr int NT = 512, BK = 128, BQ = 32, TE = tile_elems<BQ, D>();
   constexpr int KC = D / 16, DB = D / 32, PE = 4 * 2 * 64 * 8;  // 4 blocks x 2 chunks x 64 lanes x 16 B
@@ -419,8 +424,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int kb = wave & 3;                 // key block of this wave (either role)
   const int wk0 = k0 + 32 * kb, wk1 = min(wk0 + 32, a.nk);
 
-  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * a.nq * D;
-  const uint16_t* dO = (const uint16_t*)a.dout + (int64_t)bh * a.nq * D;
+  const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
+  const uint16_t* dO = (const uint16_t*)a.dout + rslice<SR, D>(a.rdo, bh, a.H, a.nq);
   const float* LSE = a.lse + (int64_t)bh * a.nq;
   const float* DS = a.dsum + (int64_t)bh * a.nq;
 
@@ -436,8 +441,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   float rstat = 0.f;
   auto fetch = [&](int j) {
     const int r0 = t0 + j * BQ;
-    rq.load(Q, r0, a.nq, tid);
-    rg.load(dO, r0, a.nq, tid);
+    rq.template load<SR>(Q, a.rq, r0, a.nq, tid);
+    rg.template load<SR>(dO, a.rdo, r0, a.nq, tid);
     // every lane loads (no branch around a load: a value loaded under a
     // divergent branch is waited for where the branch rejoins, which would
     // cancel the prefetch); only threads 0..63 store theirs
@@ -470,13 +475,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 
   if (wave < 4) {
     // ---------------------------------------------------------- score waves
-    const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
-    const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * a.nk * D;
+    const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
+    const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
     const int myk = wk0 + (lane & 31);
     const bool kvalid = myk < a.nk;
     bf16x8 kop[KC], vop[KC];
-    load_operand_rows<D>(kop, K + (int64_t)myk * D, kvalid, gq);
-    load_operand_rows<D>(vop, V + (int64_t)myk * D, kvalid, gq);
+    load_operand_rows<D>(kop, K + rrow<SR, D>(a.rk, myk), kvalid, gq);
+    load_operand_rows<D>(vop, V + rrow<SR, D>(a.rv, myk), kvalid, gq);
     const int clo = kvalid ? mg.col_lo(myk) : 0;
     const int chi = kvalid ? mg.col_hi(myk) : 0;
     const float sl2 = a.scale * kLog2e;
@@ -609,19 +614,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     uint16_t* mine = kb == 0 ? sQ0 : kb == 1 ? sG0 : kb == 2 ? sQ1 : sG1;
     acc_to_lds<D>(mine, lane & 31, dkacc, a.scale, gq);
     __syncthreads();
-    uint16_t* dK = (uint16_t*)a.dk + (int64_t)bh * a.nk * D;
-    store_tile<32, D, 256>(dK, k0, a.nk, sQ0, tid - 256);
-    store_tile<32, D, 256>(dK, k0 + 32, a.nk, sG0, tid - 256);
-    store_tile<32, D, 256>(dK, k0 + 64, a.nk, sQ1, tid - 256);
-    store_tile<32, D, 256>(dK, k0 + 96, a.nk, sG1, tid - 256);
+    uint16_t* dK = (uint16_t*)a.dk + rslice<SR, D>(a.rdk, bh, a.H, a.nk);
+    store_tile<32, D, 256, SR>(dK, a.rdk, k0, a.nk, sQ0, tid - 256);
+    store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 32, a.nk, sG0, tid - 256);
+    store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 64, a.nk, sQ1, tid - 256);
+    store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 96, a.nk, sG1, tid - 256);
     __syncthreads();
     acc_to_lds<D>(mine, lane & 31, dvacc, 1.f, gq);
     __syncthreads();
-    uint16_t* dV = (uint16_t*)a.dv + (int64_t)bh * a.nk * D;
-    store_tile<32, D, 256>(dV, k0, a.nk, sQ0, tid - 256);
-    store_tile<32, D, 256>(dV, k0 + 32, a.nk, sG0, tid - 256);
-    store_tile<32, D, 256>(dV, k0 + 64, a.nk, sQ1, tid - 256);
-    store_tile<32, D, 256>(dV, k0 + 96, a.nk, sG1, tid - 256);
+    uint16_t* dV = (uint16_t*)a.dv + rslice<SR, D>(a.rdv, bh, a.H, a.nk);
+    store_tile<32, D, 256, SR>(dV, a.rdv, k0, a.nk, sQ0, tid - 256);
+    store_tile<32, D, 256, SR>(dV, a.rdv, k0 + 32, a.nk, sG0, tid - 256);
+    store_tile<32, D, 256, SR>(dV, a.rdv, k0 + 64, a.nk, sQ1, tid - 256);
+    store_tile<32, D, 256, SR>(dV, a.rdv, k0 + 96, a.nk, sG1, tid - 256);
   }
 }
 
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 // LDS (transpose reads give K^T), each wave's dS operands (16 bytes per lane
 // per 16-key chunk, stored by the dK/dV pass in exactly this register order)
 // loaded from the workspace one key tile ahead.
-template <int D, int MODE>
+template <int D, int MODE, bool SR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_ds_kernel(BwdArgs a, int nqt) {
   constexpr int NT = 256, BM = 128, BN = 128, TE = tile_elems<BN, D>();
   constexpr int DB = D / 32, NKB = BN / 32;
@@ -645,7 +650,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   MaskGeom mg = a.mg;
   if (MODE != kAnyMask) mg.mode = MODE;
   const int i0 = qt * BM, i1 = min(i0 + BM, a.nq);
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
+  const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
   const uint16_t* DS = a.ds + (int64_t)bh * a.ds_per_bh * kDsBlockElems;
 
   const int wa = i0 + wave * 32;
@@ -694,19 +699,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   if (lo < hi) {
     bf16x8 opA[NKB][2], opB[NKB][2];
     unsigned vA = 0, vB = 0;
-    dma_tile<BN, D, NT>(sK0, K, t0, a.nk, tid);
+    dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
     fetch(opA, vA);
     __syncthreads();
     for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
       if (j0 + BN < hi) {
-        dma_tile<BN, D, NT>(sK1, K, j0 + BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid);
         fetch(opB, vB);
       }
       tile(sK0, opA, vA);
       __syncthreads();
       if (j0 + BN >= hi) break;
       if (j0 + 2 * BN < hi) {
-        dma_tile<BN, D, NT>(sK0, K, j0 + 2 * BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid);
         fetch(opA, vA);
       }
       tile(sK1, opB, vB);
@@ -715,12 +720,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   }
   acc_to_lds<D>(sK0, 32 * wave + (lane & 31), dqacc, a.scale, gq);
   __syncthreads();
-  store_tile<BM, D, NT>((uint16_t*)a.dq + (int64_t)bh * a.nq * D, i0, a.nq, sK0, tid);
+  store_tile<BM, D, NT, SR>((uint16_t*)a.dq + rslice<SR, D>(a.rdq, bh, a.H, a.nq), a.rdq, i0, a.nq,
+                            sK0, tid);
 }
 
 // ------------------------------------------------------------ backward: dQ
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, bool SR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void dq_bf16_kernel(BwdArgs a, int nqt) {
   static_assert(NW == 4, "dQ staging assumes 4 waves (two 64-row tiles)");
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, TE = tile_elems<BN, D>();
@@ -739,10 +745,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
   const int i0 = qt * BM, i1 = min(i0 + BM, a.nq);
 
-  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * a.nq * D;
-  const uint16_t* dO = (const uint16_t*)a.dout + (int64_t)bh * a.nq * D;
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
-  const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * a.nk * D;
+  const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
+  const uint16_t* dO = (const uint16_t*)a.dout + rslice<SR, D>(a.rdo, bh, a.H, a.nq);
+  const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
+  const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
 
   const int wa = i0 + wave * 32, wb = min(wa + 32, a.nq);
   const int myq = wa + (lane & 31);
@@ -757,12 +763,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int t0 = (lo / BN) * BN;
 
   if (lo < hi) {
-    dma_tile<BN, D, NT>(sK0, K, t0, a.nk, tid);
-    dma_tile<BN, D, NT>(sV0, V, t0, a.nk, tid);
+    dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
+    dma_tile<BN, D, NT, SR>(sV0, V, a.rv, t0, a.nk, tid);
   }
   bf16x8 qop[KC], dop[KC];
-  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
-  load_operand_rows<D>(dop, dO + (int64_t)myq * D, qvalid, gq);
+  load_operand_rows<D>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
+  load_operand_rows<D>(dop, dO + rrow<SR, D>(a.rdo, myq), qvalid, gq);
   const float lse2 = qvalid ? a.lse[(int64_t)bh * a.nq + myq] * kLog2e : 0.f;
   const float dsv = qvalid ? a.dsum[(int64_t)bh * a.nq + myq] : 0.f;
 
@@ -808,15 +814,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __syncthreads();
     for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
       if (j0 + BN < hi) {
-        dma_tile<BN, D, NT>(sK1, K, j0 + BN, a.nk, tid);
-        dma_tile<BN, D, NT>(sV1, V, j0 + BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sV1, V, a.rv, j0 + BN, a.nk, tid);
       }
       tile(sK0, sV0, j0);
       __syncthreads();
       if (j0 + BN >= hi) break;
       if (j0 + 2 * BN < hi) {
-        dma_tile<BN, D, NT>(sK0, K, j0 + 2 * BN, a.nk, tid);
-        dma_tile<BN, D, NT>(sV0, V, j0 + 2 * BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid);
+        dma_tile<BN, D, NT, SR>(sV0, V, a.rv, j0 + 2 * BN, a.nk, tid);
       }
       tile(sK1, sV1, j0 + BN);
       __syncthreads();
@@ -824,40 +830,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   acc_to_lds<D>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), dqacc, a.scale, gq);
   __syncthreads();
-  uint16_t* dQ = (uint16_t*)a.dq + (int64_t)bh * a.nq * D;
-  store_tile<64, D, NT>(dQ, i0, a.nq, sK0, tid);
-  store_tile<64, D, NT>(dQ, i0 + 64, a.nq, sV0, tid);
+  uint16_t* dQ = (uint16_t*)a.dq + rslice<SR, D>(a.rdq, bh, a.H, a.nq);
+  store_tile<64, D, NT, SR>(dQ, a.rdq, i0, a.nq, sK0, tid);
+  store_tile<64, D, NT, SR>(dQ, a.rdq, i0 + 64, a.nq, sV0, tid);
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool SR>
 int launch_fwd_dm(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = 4, BM = 32 * NW;
   const int nqt = (a.nq + BM - 1) / BM;
   const int64_t grid = (int64_t)nqt * a.B * a.H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kAnyMask>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a, nqt);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kAnyMask, SR>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     s, a, nqt);
   return (int)hipGetLastError();
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool SR>
 int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
   constexpr int NW = 4;
   int err = 0;
   if (passes & kPassRowSum) {
-    const int64_t rows = (int64_t)a.B * a.H * a.nq;
-    hipLaunchKernelGGL((dsum_bf16_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                       s, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dsum, rows);
+    const int nblk = (a.nq + 15) / 16;
+    hipLaunchKernelGGL((dsum_bf16_kernel<D, SR>), dim3((unsigned)((int64_t)nblk * a.B * a.H)),
+                       dim3(256), 0, s, a, nblk);
     if ((err = (int)hipGetLastError())) return err;
   }
   if (passes & kPassDKDV) {
     if constexpr (D == 128) {
       const int nkt = (a.nk + 127) / 128;
-      hipLaunchKernelGGL((dkdv_pp_kernel<D, kAnyMask>), dim3((unsigned)((int64_t)nkt * a.B * a.H)),
-                         dim3(512), 0, s, a, nkt);
+      hipLaunchKernelGGL((dkdv_pp_kernel<D, kAnyMask, SR>),
+                         dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(512), 0, s, a, nkt);
     } else {
       constexpr int BK = 32 * DkdvShape<D>::KB * NW;
       const int nkt = (a.nk + BK - 1) / BK;
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, kAnyMask>), dim3((unsigned)((int64_t)nkt * a.B * a.H)),
-                         dim3(NW * 64), 0, s, a, nkt);
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, kAnyMask, SR>),
+                         dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(NW * 64), 0, s, a, nkt);
     }
     if ((err = (int)hipGetLastError())) return err;
   }
@@ -866,14 +873,14 @@ int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
     bool done = false;
     if constexpr (D == 128) {
       if (a.ds) {
-        hipLaunchKernelGGL((dq_ds_kernel<D, MODE>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
+        hipLaunchKernelGGL((dq_ds_kernel<D, MODE, SR>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
                            dim3(256), 0, s, a, nqt);
         done = true;
       }
     }
     if (!done)
-      hipLaunchKernelGGL((dq_bf16_kernel<D, NW, MODE>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
-                         dim3(NW * 64), 0, s, a, nqt);
+      hipLaunchKernelGGL((dq_bf16_kernel<D, NW, MODE, SR>),
+                         dim3((unsigned)((int64_t)nqt * a.B * a.H)), dim3(NW * 64), 0, s, a, nqt);
     if ((err = (int)hipGetLastError())) return err;
   }
   return 0;
@@ -881,22 +888,30 @@ int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
 
 template <int D>
 int launch_fwd_d(const FwdArgs& a, hipStream_t s) {
-  return launch_fwd_dm<D, kAnyMask>(a, s);
+  if (rows_plain(a, D)) return launch_fwd_dm<D, kAnyMask, false>(a, s);
+  return launch_fwd_dm<D, kAnyMask, true>(a, s);
 }
 
 // The dQ kernel is instantiated per mask mode (measured 16% faster on the
 // causal and sliding workloads with the visibility tests folded); the forward
 // and dK/dV kernels read the mode at run time (their per-mode instances
-// measured 3-4% slower on the causal workload).
-template <int D>
-int launch_bwd_d(const BwdArgs& a, hipStream_t s, int passes) {
+// measured 3-4% slower on the causal workload).  Every kernel comes in a
+// contiguous-rows and a strided-rows instance.
+template <int D, bool SR>
+int launch_bwd_ds(const BwdArgs& a, hipStream_t s, int passes) {
   switch (a.mg.mode) {
-    case kNone: return launch_bwd_dm<D, kNone>(a, s, passes);
-    case kCausal: return launch_bwd_dm<D, kCausal>(a, s, passes);
-    case kSliding: return launch_bwd_dm<D, kSliding>(a, s, passes);
-    case kBlock: return launch_bwd_dm<D, kBlock>(a, s, passes);
+    case kNone: return launch_bwd_dm<D, kNone, SR>(a, s, passes);
+    case kCausal: return launch_bwd_dm<D, kCausal, SR>(a, s, passes);
+    case kSliding: return launch_bwd_dm<D, kSliding, SR>(a, s, passes);
+    case kBlock: return launch_bwd_dm<D, kBlock, SR>(a, s, passes);
   }
   return (int)hipErrorInvalidValue;
+}
+
+template <int D>
+int launch_bwd_d(const BwdArgs& a, hipStream_t s, int passes) {
+  return rows_plain(a, D) ? launch_bwd_ds<D, false>(a, s, passes)
+                          : launch_bwd_ds<D, true>(a, s, passes);
 }
 
 }  // namespace

@@ -62,7 +62,7 @@ __device__ __forceinline__ LocalTile local_tile(int tile, int nq, int lw, int lq
 // ------------------------------------------------------------------ forward
 
 // QR: query buffer rows (32 when QT <= 32, else 64); one wave per 32 rows
-template <int D, int QR>
+template <int D, int QR, bool SR>
 __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
   constexpr int NT = 2 * QR, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
@@ -75,17 +75,17 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int tk0 = tile * kTile;
   const LocalTile lt = local_tile(tile, a.nq, lw, lq);
 
-  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)bh * a.nq * D;
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)bh * a.nk * D;
-  const uint16_t* V = (const uint16_t*)a.v + (int64_t)bh * a.nk * D;
+  const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
+  const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
+  const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
 
-  dma_tile<kTile, D, NT>(sK, K, tk0, a.nk, tid);
-  dma_tile<kTile, D, NT>(sV, V, tk0, a.nk, tid);
+  dma_tile<kTile, D, NT, SR>(sK, K, a.rk, tk0, a.nk, tid);
+  dma_tile<kTile, D, NT, SR>(sV, V, a.rv, tk0, a.nk, tid);
   const int myr = wave * 32 + (lane & 31);  // this lane's query row in the tile
   const int myq = lt.tq0 + myr;
   const bool qvalid = lt.real(myr);
   bf16x8 qop[KC];
-  load_operand_rows<D>(qop, Q + (int64_t)myq * D, qvalid, gq);
+  load_operand_rows<D>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
   __syncthreads();
 
   f32x16 s[2];
@@ -141,14 +141,15 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
   acc_to_lds<D>(sK, myr, oacc, qvalid ? 1.f / l : 0.f, gq);
   if (qvalid && gq == 0) a.lse[(int64_t)bh * a.nq + myq] = (mb2 + log2f(l)) * kLn2;
   __syncthreads();
-  store_tile<QR, D, NT>((uint16_t*)a.o + (int64_t)bh * a.nq * D, lt.tq0, lt.qend, sK, tid);
+  uint16_t* O = (uint16_t*)a.o + rslice<SR, D>(a.ro, bh, a.H, a.nq);
+  store_tile<QR, D, NT, SR>(O, a.ro, lt.tq0, lt.qend, sK, tid);
 }
 
 // ----------------------------------------------------------------- backward
 
 // QR: query buffer rows; waves 0-1 own the tile's keys, the QR / 32 waves
 // after them its query rows
-template <int D, int QR>
+template <int D, int QR, bool SR>
 __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int ntile, int lw, int lq) {
   constexpr int NT = 128 + 2 * QR, KE = tile_elems<kTile, D>(), QE = tile_elems<QR, D>();
   constexpr int KC = D / 16, DB = D / 32, QB = QR / 32;
@@ -165,12 +166,14 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
   const int tile = blockIdx.x % ntile;
   const int tk0 = tile * kTile;
   const LocalTile lt = local_tile(tile, a.nq, lw, lq);
-  const int64_t qbase = (int64_t)bh * a.nq * D, kbase = (int64_t)bh * a.nk * D;
-
-  dma_tile<QR, D, NT>(sQ, (const uint16_t*)a.q + qbase, lt.tq0, lt.qend, tid);
-  dma_tile<kTile, D, NT>(sK, (const uint16_t*)a.k + kbase, tk0, a.nk, tid);
-  dma_tile<kTile, D, NT>(sV, (const uint16_t*)a.v + kbase, tk0, a.nk, tid);
-  dma_tile<QR, D, NT>(sG, (const uint16_t*)a.dout + qbase, lt.tq0, lt.qend, tid);
+  const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
+  const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
+  const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
+  const uint16_t* dO = (const uint16_t*)a.dout + rslice<SR, D>(a.rdo, bh, a.H, a.nq);
+  dma_tile<QR, D, NT, SR>(sQ, Q, a.rq, lt.tq0, lt.qend, tid);
+  dma_tile<kTile, D, NT, SR>(sK, K, a.rk, tk0, a.nk, tid);
+  dma_tile<kTile, D, NT, SR>(sV, V, a.rv, tk0, a.nk, tid);
+  dma_tile<QR, D, NT, SR>(sG, dO, a.rdo, lt.tq0, lt.qend, tid);
   if (tid < QR) sL[tid] = lt.real(tid) ? a.lse[(int64_t)bh * a.nq + lt.tq0 + tid] * kLog2e : 0.f;
   __syncthreads();
 
@@ -292,9 +295,12 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
     acc_to_lds<D>(sV, own, acc1, 1.f, gq);
   }
   __syncthreads();
-  store_tile<QR, D, NT>((uint16_t*)a.dq + qbase, lt.tq0, lt.qend, sQ, tid);
-  store_tile<kTile, D, NT>((uint16_t*)a.dk + kbase, tk0, a.nk, sK, tid);
-  store_tile<kTile, D, NT>((uint16_t*)a.dv + kbase, tk0, a.nk, sV, tid);
+  store_tile<QR, D, NT, SR>((uint16_t*)a.dq + rslice<SR, D>(a.rdq, bh, a.H, a.nq), a.rdq, lt.tq0,
+                            lt.qend, sQ, tid);
+  store_tile<kTile, D, NT, SR>((uint16_t*)a.dk + rslice<SR, D>(a.rdk, bh, a.H, a.nk), a.rdk, tk0,
+                               a.nk, sK, tid);
+  store_tile<kTile, D, NT, SR>((uint16_t*)a.dv + rslice<SR, D>(a.rdv, bh, a.H, a.nk), a.rdv, tk0,
+                               a.nk, sV, tid);
 }
 
 int log2_of(int w) {
@@ -318,26 +324,39 @@ LocalLaunch local_launch(const MaskGeom& g) {
   return l;
 }
 
-template <int D>
-int fwd_d(const FwdArgs& a, hipStream_t s) {
+template <int D, bool SR>
+int fwd_ds(const FwdArgs& a, hipStream_t s) {
   const LocalLaunch l = local_launch(a.mg);
   const dim3 grid((unsigned)((int64_t)l.ntile * a.B * a.H));
   if (l.wide)
-    hipLaunchKernelGGL((fwd_local_kernel<D, 64>), grid, dim3(128), 0, s, a, l.ntile, l.lw, l.lq);
+    hipLaunchKernelGGL((fwd_local_kernel<D, 64, SR>), grid, dim3(128), 0, s, a, l.ntile, l.lw,
+                       l.lq);
   else
-    hipLaunchKernelGGL((fwd_local_kernel<D, 32>), grid, dim3(64), 0, s, a, l.ntile, l.lw, l.lq);
+    hipLaunchKernelGGL((fwd_local_kernel<D, 32, SR>), grid, dim3(64), 0, s, a, l.ntile, l.lw, l.lq);
+  return (int)hipGetLastError();
+}
+
+template <int D, bool SR>
+int bwd_ds(const BwdArgs& a, hipStream_t s) {
+  const LocalLaunch l = local_launch(a.mg);
+  const dim3 grid((unsigned)((int64_t)l.ntile * a.B * a.H));
+  if (l.wide)
+    hipLaunchKernelGGL((bwd_local_kernel<D, 64, SR>), grid, dim3(256), 0, s, a, l.ntile, l.lw,
+                       l.lq);
+  else
+    hipLaunchKernelGGL((bwd_local_kernel<D, 32, SR>), grid, dim3(192), 0, s, a, l.ntile, l.lw,
+                       l.lq);
   return (int)hipGetLastError();
 }
 
 template <int D>
+int fwd_d(const FwdArgs& a, hipStream_t s) {
+  return rows_plain(a, D) ? fwd_ds<D, false>(a, s) : fwd_ds<D, true>(a, s);
+}
+
+template <int D>
 int bwd_d(const BwdArgs& a, hipStream_t s) {
-  const LocalLaunch l = local_launch(a.mg);
-  const dim3 grid((unsigned)((int64_t)l.ntile * a.B * a.H));
-  if (l.wide)
-    hipLaunchKernelGGL((bwd_local_kernel<D, 64>), grid, dim3(256), 0, s, a, l.ntile, l.lw, l.lq);
-  else
-    hipLaunchKernelGGL((bwd_local_kernel<D, 32>), grid, dim3(192), 0, s, a, l.ntile, l.lw, l.lq);
-  return (int)hipGetLastError();
+  return rows_plain(a, D) ? bwd_ds<D, false>(a, s) : bwd_ds<D, true>(a, s);
 }
 
 }  // namespace

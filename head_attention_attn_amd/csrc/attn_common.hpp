@@ -129,6 +129,49 @@ struct MaskGeom {
 // elements of one dS block: 2 key chunks x 64 lanes x 8 bf16
 constexpr int kDsBlockElems = 1024;
 
+// ---------------------------------------------------------------- row maps
+
+// Where the rows of one [B][H][N][d] tensor live.  Row j (token j) of slice
+// (b, h) starts at element
+//     b * batch + h * head + (j >> wshift) * win + (j & wmask) * tok
+// of the tensor's base pointer, and its d values are contiguous.  A tensor
+// in one window per slice (every contiguous layout, and any strided one whose
+// windows follow each other at a uniform token stride) has wshift = 31,
+// wmask = 0x7fffffff, win = 0.  The host guarantees that the in-slice offset
+// of every row fits in 31 bits.
+struct RowMap {
+  int64_t batch, head;
+  int32_t win, tok;
+  int32_t wshift, wmask;
+
+  // element offset of slice bh = b * H + h
+  ATTN_HD int64_t slice(int bh, int H) const {
+    return (int64_t)(bh / H) * batch + (int64_t)(bh % H) * head;
+  }
+  // element offset of row j inside its slice
+  ATTN_HD uint32_t row(int j) const {
+    return (uint32_t)(j >> wshift) * (uint32_t)win + (uint32_t)(j & wmask) * (uint32_t)tok;
+  }
+  // the contiguous layout of an [H][n][d] slice set: row j at j * d
+  ATTN_HD bool plain(int H, int n, int d) const {
+    return wshift == 31 && tok == d && batch == (int64_t)H * n * d && head == (int64_t)n * d;
+  }
+};
+
+// Row addressing for kernels compiled per layout class: SR = false is the
+// contiguous layout (slice bh at bh * n * D, row j at j * D, both folded at
+// compile time), SR = true reads the RowMap.
+template <bool SR, int D>
+ATTN_HD uint32_t rrow(const RowMap& m, int j) {
+  if constexpr (SR) return m.row(j);
+  else return (uint32_t)j * D;
+}
+template <bool SR, int D>
+ATTN_HD int64_t rslice(const RowMap& m, int bh, int H, int n) {
+  if constexpr (SR) return m.slice(bh, H);
+  else return (int64_t)bh * n * D;
+}
+
 // ---------------------------------------------------------------- launches
 
 struct FwdArgs {
@@ -136,7 +179,8 @@ struct FwdArgs {
   const void* k;
   const void* v;
   void* o;
-  float* lse;
+  float* lse;  // [B][H][Nq], contiguous
+  RowMap rq, rk, rv, ro;
   int B, H, nq, nk;
   float scale;
   MaskGeom mg;
@@ -152,6 +196,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
+  RowMap rq, rk, rv, ro, rdo, rdq, rdk, rdv;
   float* dsum;  // workspace: D_i = sum_c dO[i][c] * O[i][c], fp32 [B][H][Nq]
   // optional workspace part: dS blocks written by the dK/dV pass and read by
   // the dQ pass instead of recomputing S and dP (null: recompute);
@@ -162,6 +207,17 @@ struct BwdArgs {
   float scale;
   MaskGeom mg;
 };
+
+// every tensor of a call in the contiguous layout (the SR = false kernels)
+inline bool rows_plain(const FwdArgs& a, int d) {
+  return a.rq.plain(a.H, a.nq, d) && a.rk.plain(a.H, a.nk, d) && a.rv.plain(a.H, a.nk, d) &&
+         a.ro.plain(a.H, a.nq, d);
+}
+inline bool rows_plain(const BwdArgs& a, int d) {
+  return a.rq.plain(a.H, a.nq, d) && a.rk.plain(a.H, a.nk, d) && a.rv.plain(a.H, a.nk, d) &&
+         a.ro.plain(a.H, a.nq, d) && a.rdo.plain(a.H, a.nq, d) && a.rdq.plain(a.H, a.nq, d) &&
+         a.rdk.plain(a.H, a.nk, d) && a.rdv.plain(a.H, a.nk, d);
+}
 
 // backward pass bits (the values of include/attn.h's ATTN_PASS_*)
 enum BwdPass : int { kPassRowSum = 1, kPassDKDV = 2, kPassDQ = 4, kPassAll = 7 };

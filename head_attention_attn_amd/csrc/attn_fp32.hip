@@ -48,46 +48,46 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
   const int64_t rows = (int64_t)a.B * a.H * a.nq;
   if (row >= rows) return;  // whole 16-lane groups leave together
-  const int64_t bh = row / a.nq;
+  const int bh = (int)(row / a.nq);
   const int i = (int)(row % a.nq);
-  const float* K = (const float*)a.k + bh * a.nk * D;
-  const float* V = (const float*)a.v + bh * a.nk * D;
+  const float* K = (const float*)a.k + a.rk.slice(bh, a.H);
+  const float* V = (const float*)a.v + a.rv.slice(bh, a.H);
   float q[E], acc[E];
-  load_slice<D>(q, (const float*)a.q + row * D, li);
+  load_slice<D>(q, (const float*)a.q + a.rq.slice(bh, a.H) + a.rq.row(i), li);
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
   const int lo = a.mg.row_lo(i), hi = a.mg.row_hi(i);
   for (int j = lo; j < hi; ++j) {
-    const float s = a.scale * dot_slice<D>(q, K + (int64_t)j * D, li);
+    const float s = a.scale * dot_slice<D>(q, K + a.rk.row(j), li);
     const float mnew = fmaxf(m, s);
     const float alpha = expf(m - mnew);   // m = -inf on the first key -> 0
     const float p = expf(s - mnew);
     l = l * alpha + p;
-    const float* vr = V + (int64_t)j * D;
+    const float* vr = V + a.rv.row(j);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = fmaf(p, vr[li + kGroup * e], acc[e] * alpha);
     m = mnew;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* O = (float*)a.o + row * D;
+  float* O = (float*)a.o + a.ro.slice(bh, a.H) + a.ro.row(i);
 #pragma unroll
   for (int e = 0; e < E; ++e) O[li + kGroup * e] = acc[e] * inv;
   if (li == 0) a.lse[row] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void dsum_fp32_kernel(const float* __restrict__ o,
-                                                        const float* __restrict__ dout,
-                                                        float* __restrict__ dsum, int64_t rows) {
+__global__ __launch_bounds__(256) void dsum_fp32_kernel(BwdArgs a) {
   constexpr int E = D / kGroup;
   const int li = threadIdx.x & (kGroup - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
-  if (row >= rows) return;
+  if (row >= (int64_t)a.B * a.H * a.nq) return;
+  const int bh = (int)(row / a.nq);
+  const int i = (int)(row % a.nq);
   float x[E];
-  load_slice<D>(x, o + row * D, li);
-  const float s = dot_slice<D>(x, dout + row * D, li);
-  if (li == 0) dsum[row] = s;
+  load_slice<D>(x, (const float*)a.o + a.ro.slice(bh, a.H) + a.ro.row(i), li);
+  const float s = dot_slice<D>(x, (const float*)a.dout + a.rdo.slice(bh, a.H) + a.rdo.row(i), li);
+  if (li == 0) a.dsum[row] = s;
 }
 
 template <int D>
@@ -97,25 +97,25 @@ __global__ __launch_bounds__(256) void dq_fp32_kernel(BwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
   const int64_t rows = (int64_t)a.B * a.H * a.nq;
   if (row >= rows) return;
-  const int64_t bh = row / a.nq;
+  const int bh = (int)(row / a.nq);
   const int i = (int)(row % a.nq);
-  const float* K = (const float*)a.k + bh * a.nk * D;
-  const float* V = (const float*)a.v + bh * a.nk * D;
+  const float* K = (const float*)a.k + a.rk.slice(bh, a.H);
+  const float* V = (const float*)a.v + a.rv.slice(bh, a.H);
   float q[E], g[E], acc[E];
-  load_slice<D>(q, (const float*)a.q + row * D, li);
-  load_slice<D>(g, (const float*)a.dout + row * D, li);
+  load_slice<D>(q, (const float*)a.q + a.rq.slice(bh, a.H) + a.rq.row(i), li);
+  load_slice<D>(g, (const float*)a.dout + a.rdo.slice(bh, a.H) + a.rdo.row(i), li);
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   const float lse = a.lse[row], dsv = a.dsum[row];
   const int lo = a.mg.row_lo(i), hi = a.mg.row_hi(i);
   for (int j = lo; j < hi; ++j) {
-    const float* kr = K + (int64_t)j * D;
+    const float* kr = K + a.rk.row(j);
     const float p = expf(a.scale * dot_slice<D>(q, kr, li) - lse);
-    const float ds = p * (dot_slice<D>(g, V + (int64_t)j * D, li) - dsv);
+    const float ds = p * (dot_slice<D>(g, V + a.rv.row(j), li) - dsv);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, kr[li + kGroup * e], acc[e]);
   }
-  float* dQ = (float*)a.dq + row * D;
+  float* dQ = (float*)a.dq + a.rdq.slice(bh, a.H) + a.rdq.row(i);
 #pragma unroll
   for (int e = 0; e < E; ++e) dQ[li + kGroup * e] = acc[e] * a.scale;
 }
@@ -127,21 +127,21 @@ __global__ __launch_bounds__(256) void dkdv_fp32_kernel(BwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kGroup);
   const int64_t rows = (int64_t)a.B * a.H * a.nk;
   if (row >= rows) return;
-  const int64_t bh = row / a.nk;
+  const int bh = (int)(row / a.nk);
   const int j = (int)(row % a.nk);
-  const float* Q = (const float*)a.q + bh * a.nq * D;
-  const float* dO = (const float*)a.dout + bh * a.nq * D;
-  const float* LSE = a.lse + bh * a.nq;
-  const float* DS = a.dsum + bh * a.nq;
+  const float* Q = (const float*)a.q + a.rq.slice(bh, a.H);
+  const float* dO = (const float*)a.dout + a.rdo.slice(bh, a.H);
+  const float* LSE = a.lse + (int64_t)bh * a.nq;
+  const float* DS = a.dsum + (int64_t)bh * a.nq;
   float k[E], v[E], dk[E], dv[E];
-  load_slice<D>(k, (const float*)a.k + row * D, li);
-  load_slice<D>(v, (const float*)a.v + row * D, li);
+  load_slice<D>(k, (const float*)a.k + a.rk.slice(bh, a.H) + a.rk.row(j), li);
+  load_slice<D>(v, (const float*)a.v + a.rv.slice(bh, a.H) + a.rv.row(j), li);
 #pragma unroll
   for (int e = 0; e < E; ++e) dk[e] = dv[e] = 0.f;
   const int lo = a.mg.col_lo(j), hi = a.mg.col_hi(j);
   for (int i = lo; i < hi; ++i) {
-    const float* qr = Q + (int64_t)i * D;
-    const float* gr = dO + (int64_t)i * D;
+    const float* qr = Q + a.rq.row(i);
+    const float* gr = dO + a.rdo.row(i);
     const float p = expf(a.scale * dot_slice<D>(k, qr, li) - LSE[i]);
     const float ds = p * (dot_slice<D>(v, gr, li) - DS[i]);
 #pragma unroll
@@ -150,8 +150,8 @@ __global__ __launch_bounds__(256) void dkdv_fp32_kernel(BwdArgs a) {
       dk[e] = fmaf(ds, qr[li + kGroup * e], dk[e]);
     }
   }
-  float* dK = (float*)a.dk + row * D;
-  float* dV = (float*)a.dv + row * D;
+  float* dK = (float*)a.dk + a.rdk.slice(bh, a.H) + a.rdk.row(j);
+  float* dV = (float*)a.dv + a.rdv.slice(bh, a.H) + a.rdv.row(j);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     dK[li + kGroup * e] = dk[e] * a.scale;
@@ -175,8 +175,7 @@ int bwd_d(const BwdArgs& a, hipStream_t s, int passes) {
   const int64_t qrows = (int64_t)a.B * a.H * a.nq, krows = (int64_t)a.B * a.H * a.nk;
   int err = 0;
   if (passes & kPassRowSum) {
-    hipLaunchKernelGGL((dsum_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s,
-                       (const float*)a.o, (const float*)a.dout, a.dsum, qrows);
+    hipLaunchKernelGGL((dsum_fp32_kernel<D>), dim3(blocks_for(qrows)), dim3(256), 0, s, a);
     if ((err = (int)hipGetLastError())) return err;
   }
   if (passes & kPassDKDV) {

@@ -88,24 +88,26 @@ __device__ __forceinline__ bf16x8 lds_tr8(const uint16_t* tile, int r0, int c0, 
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Direct global -> LDS load of a ROWS x D bf16 tile (rows r0 .. r0+ROWS-1 of a
-// [n][D] matrix) into the tile layout, by NT threads.  gfx950's
+// Direct global -> LDS load of a ROWS x D bf16 tile (rows r0 .. r0+ROWS-1 of
+// the n rows of a slice, addressed through `rm` from the slice base `src`)
+// into the tile layout, by NT threads.  gfx950's
 // global_load_lds_dwordx4 puts the 16 bytes each lane loads at the wave's LDS
 // base + 16 * lane, with no register staging: lane slot p is LDS chunk
 // position p, so the lane fetches the logical chunk that the layout stores
 // there; lanes on padding slots are switched off.  Rows >= n are filled from
 // row n - 1 (finite values that every kernel masks out).  The loads count on
 // vmcnt; the caller waits for them (__syncthreads() does) before reading.
-template <int ROWS, int D, int NT>
-__device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, int r0, int n,
-                                         int tid) {
+template <int ROWS, int D, int NT, bool SR>
+__device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, const RowMap& rm,
+                                         int r0, int n, int tid) {
   constexpr int CPR = D / 8, SPR = tstride<D>() / 8, TOTAL = ROWS * SPR;
   static_assert(TOTAL % 64 == 0, "whole waves per tile");
   constexpr int STEPS = (TOTAL + NT - 1) / NT;
   // uniform base plus a 32-bit per-lane offset (the scalar-base addressing
   // form of the load: one address VGPR per load instead of two)
-  const uint16_t* base = src + (int64_t)r0 * D;
-  const int last = n - 1 - r0;
+  // contiguous rows: the tile's first row goes into the scalar base
+  const uint16_t* base = SR ? src : src + (int64_t)r0 * D;
+  const int last = SR ? n - 1 : n - 1 - r0;
 #pragma unroll
   for (int t = 0; t < STEPS; ++t) {
     const int wbase = t * NT + (tid & ~63);  // first slot of this wave's 64
@@ -114,7 +116,8 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, int
       const int row = p / SPR, phys = p % SPR;
       if (phys < CPR) {
         const int ch = phys ^ ((row >> 2) & 3);
-        const uint32_t off = (uint32_t)(min(row, last) * (2 * D) + ch * 16);  // bytes
+        const uint32_t off = SR ? 2u * rm.row(min(r0 + row, last)) + (uint32_t)(ch * 16)
+                                : (uint32_t)(min(row, last) * (2 * D) + ch * 16);  // bytes
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)((const char*)base + off),
             (__attribute__((address_space(3))) void*)(lds + wbase * 8), 16, 0, 0);
@@ -155,18 +158,22 @@ __device__ __forceinline__ int64_t ds_offset(const MaskGeom& mg, int kb, int lan
 // the two does not wait for the global loads (a barrier waits for LDS
 // traffic only), so a tile can be fetched a whole pipeline step before it is
 // written.  Rows >= n read as row n - 1 (finite values the kernels mask).
+// Rows are addressed through `rm` from the slice base `src`.
 template <int ROWS, int D, int NT>
 struct RegTile {
   static constexpr int CPR = D / 8, TOTAL = ROWS * CPR, CH = (TOTAL + NT - 1) / NT;
   uint4 r[CH];
 
-  __device__ __forceinline__ void load(const uint16_t* src, int r0, int n, int tid) {
+  template <bool SR>
+  __device__ __forceinline__ void load(const uint16_t* src, const RowMap& rm, int r0, int n,
+                                       int tid) {
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
       const int c = tid + t * NT;
       if (TOTAL % NT == 0 || c < TOTAL) {
         const int row = min(r0 + c / CPR, n - 1);
-        r[t] = *reinterpret_cast<const uint4*>(src + (int64_t)row * D + (c % CPR) * 8);
+        r[t] = *reinterpret_cast<const uint4*>(src + (SR ? (int64_t)rm.row(row) : (int64_t)row * D) +
+                                               (c % CPR) * 8);
       }
     }
   }
@@ -225,19 +232,21 @@ __device__ __forceinline__ void acc_to_lds(uint16_t* tile, int row, const f32x16
                       acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
 }
 
-// LDS -> global copy of a ROWS x D tile to rows r0 .. of a [n][D]
-// matrix by NT threads, 16 bytes per lane per step on consecutive addresses;
-// rows >= n are not written.
-template <int ROWS, int D, int NT>
-__device__ __forceinline__ void store_tile(uint16_t* dst, int r0, int n, const uint16_t* lds,
-                                           int tid) {
+// LDS -> global copy of a ROWS x D tile to rows r0 .. of the n rows of a
+// slice (slice base `dst`, rows addressed through `rm`) by NT threads, 16
+// bytes per lane per step, consecutive lanes on consecutive addresses of a
+// row; rows >= n are not written.
+template <int ROWS, int D, int NT, bool SR>
+__device__ __forceinline__ void store_tile(uint16_t* dst, const RowMap& rm, int r0, int n,
+                                           const uint16_t* lds, int tid) {
   constexpr int CPR = D / 8, TOTAL = ROWS * CPR, CH = (TOTAL + NT - 1) / NT;
 #pragma unroll
   for (int t = 0; t < CH; ++t) {
     const int c = tid + t * NT;
     const int row = c / CPR, col = (c % CPR) * 8;
     if (c < TOTAL && r0 + row < n)
-      *reinterpret_cast<uint4*>(dst + (int64_t)(r0 + row) * D + col) =
+      *reinterpret_cast<uint4*>(dst + (SR ? (int64_t)rm.row(r0 + row) : (int64_t)(r0 + row) * D) +
+                                col) =
           *reinterpret_cast<const uint4*>(lds + toff<D>(row, col));
   }
 }

@@ -27,8 +27,9 @@
  *     (output storage aliasing a cached buffer; base pointer alignment;
  *     rejecting unsupported devices up front instead of failing mid-run).
  *
- * Layouts (all tensors contiguous, row-major, element type `dtype` except lse
- * and the workspace, which are fp32):
+ * Layouts (contiguous, row-major -- the *_strided entry points below take
+ * other row strides; element type `dtype` except lse and the workspace,
+ * which are fp32):
  *     Q, O, dO, dQ : [B][H][Nq][d]
  *     K, V, dK, dV : [B][H][Nk][d]
  *     lse          : [B][H][Nq]      natural-log logsumexp of the scaled,
@@ -232,6 +233,97 @@ ATTN_API int attn_check_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t
                    const float* lse, const void* dout,
                    const void* dq, const void* dk, const void* dv,
                    const void* workspace, size_t workspace_bytes);
+
+/*
+ * Strided tensors.  The entry points above take contiguous tensors; the
+ * *_strided ones below take, for each [B][H][N][d] tensor, where its rows
+ * are: row j of slice (b, h) -- token j, counted window by window for
+ * ATTN_MASK_BLOCK -- begins at element
+ *     b * batch + h * head + (j / T) * window + (j % T) * token
+ * of the tensor's base pointer, and its d elements are contiguous.  T is the
+ * tensor's window length: for ATTN_MASK_BLOCK, `window` keys (K, V, dK, dV)
+ * or Wq = Nq / (Nk / window) query rows (Q, O, dO, dQ); for the other masks
+ * the whole sequence (one window: the `window` stride is not used).
+ *
+ * This reads Hiera's token order in place: MaskUnitAttentionFast views its
+ * qkv projection as (B, T, nw, 3, H, D), token n = t * nw + w, window index
+ * fastest ("hiera-optim 0.1.0" sdist, mask_unit.py,
+ * MaskUnitAttentionFast.forward), then permutes and copies it into
+ * (B * nw, H, T, D).  With batch = N*3*H*D, head = D, window = 3*H*D and
+ * token = nw*3*H*D, and K and V at H*D and 2*H*D past Q in the same buffer,
+ * the kernels read that projection output directly; O can be written in the
+ * same order (its own strides), ready for the output projection.
+ *
+ * Requirements: strides >= 0 and <= 2^48; the rows of a tensor nest --
+ * ordering its dimensions of extent > 1 by stride, the smallest stride is
+ * >= d and each next stride is >= the previous stride times its extent (no
+ * two rows of one tensor overlap); the last row of a slice ends within 2^31
+ * elements of the slice's first (ATTN_ERR_INVALID_ARG otherwise).  Strides
+ * of dimensions with extent > 1 are multiples of 16 bytes
+ * (ATTN_ERR_MISALIGNED otherwise).  A block layout whose windows do not
+ * follow each other at the token stride (window != T * token, more than one
+ * window) needs T to be a power of two (ATTN_ERR_UNSUPPORTED otherwise).
+ * lse and the workspace stay contiguous.  Inputs may overlap each other
+ * (q, k, v as views of one qkv buffer); outputs may not overlap inputs or
+ * each other (ATTN_ERR_ALIAS).  Two tensors with the same strides and
+ * extents -- interleaved views of one buffer, such as dq, dk, dv in one dqkv
+ * buffer -- are checked element-exactly; any other pair by address range.
+ */
+typedef struct attn_layout {
+  int64_t batch, head, window, token; /* element strides */
+} attn_layout;
+
+typedef struct attn_layouts {
+  attn_layout q, k, v, o;       /* forward and backward */
+  attn_layout dout, dq, dk, dv; /* backward only */
+} attn_layouts;
+
+/*
+ * attn_layouts_contiguous -- the layouts the contiguous entry points use
+ * (batch = H*N*d, head = N*d, window = T*d, token = d per tensor) into *out.
+ * Returns ATTN_OK, or ATTN_ERR_INVALID_ARG for a null `out` or a geometry
+ * attn_fwd would reject.
+ */
+ATTN_API int attn_layouts_contiguous(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                     int mask, int64_t window, attn_layouts* out);
+
+/*
+ * attn_fwd_strided -- attn_fwd with q, k, v, o at `layouts` (q, k, v, o
+ * members; NULL = contiguous).  Validation, results and launch behaviour are
+ * those of attn_fwd.
+ */
+ATTN_API int attn_fwd_strided(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                              float scale, int mask, int64_t window,
+                              const void* q, const void* k, const void* v,
+                              void* o, float* lse, const attn_layouts* layouts, void* stream);
+
+/*
+ * attn_bwd_strided -- attn_bwd_passes with every tensor at `layouts` (NULL =
+ * contiguous).  The workspace sizes are those of the contiguous case.
+ */
+ATTN_API int attn_bwd_strided(int passes, int dtype, int64_t B, int64_t H, int64_t Nq,
+                              int64_t Nk, int64_t d, float scale, int mask, int64_t window,
+                              const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout,
+                              void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes,
+                              const attn_layouts* layouts, void* stream);
+
+/* attn_check_fwd_strided / attn_check_bwd_strided -- their validation alone,
+ * as attn_check_fwd / attn_check_bwd. */
+ATTN_API int attn_check_fwd_strided(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                    int64_t d, float scale, int mask, int64_t window,
+                                    const void* q, const void* k, const void* v,
+                                    const void* o, const float* lse,
+                                    const attn_layouts* layouts);
+
+ATTN_API int attn_check_bwd_strided(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                    int64_t d, float scale, int mask, int64_t window,
+                                    const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout,
+                                    const void* dq, const void* dk, const void* dv,
+                                    const void* workspace, size_t workspace_bytes,
+                                    const attn_layouts* layouts);
 
 /* attn_status_string -- static, human-readable name of a status code. */
 ATTN_API const char* attn_status_string(int status);

@@ -33,7 +33,10 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_passes", "attn_bwd_fused",
                                          "attn_bwd_workspace_size", "attn_bwd_workspace_size_ds",
-                                         "attn_check_fwd", "attn_check_bwd", "attn_status_string"])
+                                         "attn_check_fwd", "attn_check_bwd", "attn_status_string",
+                                         "attn_layouts_contiguous", "attn_fwd_strided",
+                                         "attn_bwd_strided", "attn_check_fwd_strided",
+                                         "attn_check_bwd_strided"])
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -39,19 +39,25 @@ def test_autograd_gradients_match_oracle(dtype, d, mask, window, n):
             amax_rel=2.0 ** -8 if dtype == "bf16" else 0.0)
 
 
-def test_module_inside_a_graph():
+@pytest.mark.parametrize("copy", [True, False])
+def test_module_inside_a_graph(copy):
     """x -> q, k, v by a linear map -> FusedAttention -> mean: the gradient of
     the linear map's weight matches the same graph with the oracle's attention
     gradient chained by hand (dW = sum over rows of x^T [dQ dK dV] for the
-    per-head split used here)."""
+    per-head split used here).  ``copy``: q, k, v made contiguous first, or
+    read in place as strided views of the projection output."""
     torch.manual_seed(0)
     B, H, N, d = 1, 2, 130, 64
     x = torch.randn(B, N, H * d)
     w = torch.randn(H * d, 3 * H * d) * (H * d) ** -0.5
     xd, wd = x.cuda(), w.cuda().requires_grad_(True)
-    qkv = (xd @ wd).view(B, N, 3, H, d).permute(2, 0, 3, 1, 4).contiguous()
+    qkv = (xd @ wd).view(B, N, 3, H, d).permute(2, 0, 3, 1, 4)
+    if copy:
+        qkv = qkv.contiguous()
     layer = attn.FusedAttention(mask="causal")
-    o = layer(qkv[0].contiguous(), qkv[1].contiguous(), qkv[2].contiguous())
+    q, k, v = (qkv[i].contiguous() if copy else qkv[i] for i in range(3))
+    assert copy or not q.is_contiguous()
+    o = layer(q, k, v)
     o.mean().backward()
     torch.cuda.synchronize()
     # oracle: same graph in fp64 on the CPU, attention gradient from the oracle
@@ -63,4 +69,29 @@ def test_module_inside_a_graph():
     dqkv = np.stack([dq, dk, dv])                                  # [3, B, H, N, d]
     dflat = dqkv.transpose(1, 3, 0, 2, 4).reshape(B * N, 3 * H * d)
     rdw = x64.reshape(B * N, H * d).T @ dflat
-    compare([("dW", to64(wd.grad), rdw)], "fp32", "module graph", tol=(1e-5, 1e-5, 0))
+    compare([("dW", to64(wd.grad), rdw)], "fp32", f"module graph copy={copy}", tol=(1e-5, 1e-5, 0))
+
+
+def test_autograd_window_split_views():
+    """Window-split [B, nw, H, T, d] views of a token-order qkv tensor (the
+    block mask with window T) through the autograd function: the gradients
+    reaching the qkv tensor, taken back to window-major order, match the
+    oracle."""
+    B, nw, T, H, d = 2, 5, 64, 2, 64
+    q, k, v, do = make_inputs(B, H, nw * T, nw * T, d, "bf16", seed=23)
+    qkv = torch.zeros((B, T, nw, 3, H, d), dtype=torch.bfloat16, device="cuda")
+    for i, t in enumerate((q, k, v)):
+        qkv[:, :, :, i] = t.view(B, H, nw, T, d).permute(0, 3, 2, 1, 4).cuda()
+    qkv.requires_grad_(True)
+    views = [qkv[:, :, :, i].permute(0, 2, 3, 1, 4) for i in range(3)]
+    o = attn.fused_attention(*views)                               # [B, nw, H, T, d]
+    do5 = do.cuda().view(B, H, nw, T, d).permute(0, 2, 1, 3, 4)
+    (o.float() * do5.float()).sum().backward()
+    torch.cuda.synchronize()
+    g = qkv.grad.permute(3, 0, 4, 2, 1, 5).reshape(3, B, H, nw * T, d)   # window-major tokens
+    o4 = o.permute(0, 2, 1, 3, 4).reshape(B, H, nw * T, d)
+    scale = d ** -0.5
+    ro, _ = oracle_fwd(to64(q), to64(k), to64(v), scale, "block", T)
+    rdq, rdk, rdv = oracle_bwd(to64(q), to64(k), to64(v), to64(do), scale, "block", T)
+    compare([("O", to64(o4), ro), ("dQ", to64(g[0]), rdq), ("dK", to64(g[1]), rdk),
+             ("dV", to64(g[2]), rdv)], "bf16", "autograd window-split")
