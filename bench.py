@@ -142,6 +142,83 @@ def stored_traffic(workload: str, kernel: str):
     return float(val) if val is not None else None
 
 
+# ------------------------------------------------------- Hiera token order
+
+def token_order_timing(attn, torch, w, q, k, v, do, ws, kw, fused, o_ref, lse_ref, dq_ref, dk_ref,
+                       dv_ref, steps, dev):
+    """The block-mask step with its tensors in Hiera's token order (token
+    n = t * nw + w, window index fastest): K and V interleaved in one
+    (B, T, nw, 3, H, d) projection buffer, Q and dO in (B, Tq, nw, H, d)
+    buffers, O and dQ written in that order and dK, dV into one interleaved
+    (B, T, nw, 2, H, d) buffer -- read and written in place through the
+    strided entry points.  Against it, the same step on the contiguous
+    window-major layout plus the copies into and out of it that a caller
+    without strided kernels makes."""
+    B, H, d = w.B, w.H, w.d
+    nw = w.Nk // w.window
+    T, Tq = w.window, w.Nq // nw
+    qkv = torch.empty((B, T, nw, 3, H, d), dtype=q.dtype, device=dev)
+    qbuf = torch.empty((B, Tq, nw, H, d), dtype=q.dtype, device=dev)
+    gbuf = torch.empty_like(qbuf)
+    obuf, dqbuf = torch.empty_like(qbuf), torch.empty_like(qbuf)
+    dkv = torch.empty((B, T, nw, 2, H, d), dtype=q.dtype, device=dev)
+
+    def split(buf, slot=None):            # [B, nw, H, T, d] view
+        x = buf if slot is None else buf[:, :, :, slot]
+        return x.permute(0, 2, 3, 1, 4)
+
+    def windows(x4, t):                   # [B, H, nw*t, d] -> [B, nw, H, t, d] view
+        return x4.view(B, H, nw, t, d).permute(0, 2, 1, 3, 4)
+
+    q5, g5, o5, dq5 = split(qbuf), split(gbuf), split(obuf), split(dqbuf)
+    k5, v5, dk5, dv5 = split(qkv, 1), split(qkv, 2), split(dkv, 0), split(dkv, 1)
+    q5.copy_(windows(q, Tq))
+    g5.copy_(windows(do, Tq))
+    k5.copy_(windows(k, T))
+    v5.copy_(windows(v, T))
+    skw = dict(scale=w.scale)
+
+    def strided_step():
+        attn.fwd(q5, k5, v5, out=o5, lse=lse_t, **skw)
+        attn.bwd(q5, k5, v5, o5, lse_t, g5, workspace=ws, dq=dq5, dk=dk5, dv=dv5, **skw)
+
+    qc, kc, vc, gc = (torch.empty_like(t) for t in (q, k, v, do))
+    oc, dqc, dkc, dvc = (torch.empty_like(t) for t in (q, q, k, v))
+    lse_t = torch.empty_like(lse_ref)
+    lse_c = torch.empty_like(lse_ref)
+
+    def copy_step():
+        for dst, src, t in ((qc, q5, Tq), (kc, k5, T), (vc, v5, T), (gc, g5, Tq)):
+            windows(dst, t).copy_(src)
+        attn.fwd(qc, kc, vc, out=oc, lse=lse_c, **kw)
+        attn.bwd(qc, kc, vc, oc, lse_c, gc, workspace=ws, dq=dqc, dk=dkc, dv=dvc, **kw)
+        for dst, src, t in ((o5, oc, Tq), (dq5, dqc, Tq), (dk5, dkc, T), (dv5, dvc, T)):
+            dst.copy_(windows(src, t))
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / steps
+
+    t_strided = timed(strided_step)
+    same = all(torch.equal(a.permute(0, 2, 1, 3, 4).reshape(b.shape), b)
+               for a, b in ((o5, o_ref), (dq5, dq_ref), (dk5, dk_ref), (dv5, dv_ref)))
+    same = same and torch.equal(lse_t, lse_ref)
+    t_copy = timed(copy_step)
+    log(f"[bench] token order: {t_strided:.4f} ms/step in place, {t_copy:.4f} with layout copies")
+    return {"ms_per_step": round(t_strided, 5), "with_layout_copies_ms": round(t_copy, 5),
+            "steps": steps, "bitwise_equal": bool(same),
+            "layout": "K, V in a (B, T, nw, 3, H, d) buffer; Q, dO, O, dQ in (B, Tq, nw, H, d); "
+                      "dK, dV in (B, T, nw, 2, H, d)"}
+
+
 # ---------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(w, host_inputs, pairs_per_bh, budget_s: float, gpu_out):
@@ -215,6 +292,11 @@ def main() -> int:
     ap.add_argument("--autograd-steps", type=int, default=20,
                     help="after the timed region, time this many steps through the "
                          "torch.autograd wrapper (0 skips it)")
+    ap.add_argument("--layout-steps", type=int, default=20,
+                    help="block mask only: after the timed region, time this many steps "
+                         "with every tensor in Hiera's token order (strided entry points), "
+                         "and the same step done by copying to and from the contiguous "
+                         "layout (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run a plain device copy of this "
                          "many MiB 5 times (a known-size reference for HBM counters)")
@@ -315,6 +397,11 @@ def main() -> int:
         log(f"[bench] autograd wrapper: {ag_ms:.4f} ms/step")
         del qa, ka, va
 
+    layout_rec = None
+    if args.layout_steps > 0 and w.mask == "block":
+        layout_rec = token_order_timing(attn, torch, w, q, k, v, do, ws, kw, fused, o, lse, dq, dk,
+                                        dv, args.layout_steps, dev)
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.randn(n, device=dev)
@@ -399,12 +486,13 @@ def main() -> int:
         "cpu_baseline": cpu,
         "parity": parity,
         "autograd": autograd_rec,
+        "token_order": layout_rec,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count, "torch": torch.__version__,
                    "hip": torch.version.hip},
     }
     print(json.dumps(rec), flush=True)
-    ok = same and parity.get("pass", True)
+    ok = same and parity.get("pass", True) and (layout_rec is None or layout_rec["bitwise_equal"])
     return 0 if ok else 1
 
 
