@@ -30,6 +30,7 @@ path runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -44,7 +45,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 (and fp16) MFMA, AMD published
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 KERNELS = ("fwd", "rowsum", "dkdv", "dq")
@@ -91,7 +92,7 @@ def kernel_work(w, pairs_per_bh: int, kept_ds: bool = False) -> dict:
     kernel must read or write, once.  With ``kept_ds`` the dK/dV pass also
     writes dS (bf16, 2 bytes per visible pair) and the dQ pass reads dS and K
     only, instead of Q, dO, lse, D, K and V."""
-    es = 2 if w.dtype == "bf16" else 4
+    es = 4 if w.dtype == "fp32" else 2
     bh = w.B * w.H
     q_rows, k_rows, d = bh * w.Nq, bh * w.Nk, w.d
     pairs = bh * pairs_per_bh
@@ -233,7 +234,7 @@ def cpu_baseline(w, host_inputs, pairs_per_bh, budget_s: float, gpu_out):
     flop_per_bh = 14 * w.d * pairs_per_bh
     worst = {}
     done, spent = 0, 0.0
-    tol = (2e-2, 5e-3) if w.dtype == "bf16" else (1e-5, 1e-5)
+    tol = {"bf16": (2e-2, 5e-3), "fp16": (2.5e-3, 6.25e-4), "fp32": (1e-5, 1e-5)}[w.dtype]
     total_bh = w.B * w.H
     # spread the sampled slices over the batch: first, last, then every 7th
     # index, then the rest, until the time budget is spent
@@ -287,6 +288,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="block_local_hiera")
+    ap.add_argument("--dtype", choices=("bf16", "fp16"), default=None,
+                    help="run a 16-bit workload in this element type instead")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline (0 skips it)")
     ap.add_argument("--autograd-steps", type=int, default=20,
@@ -316,6 +319,11 @@ def main() -> int:
         log("no GPU visible")
         return 1
     w = WORKLOADS[args.workload]
+    if args.dtype is not None:
+        if (w.dtype == "fp32") != (args.dtype == "fp32"):
+            log("--dtype switches between the 16-bit types only")
+            return 2
+        w = dataclasses.replace(w, dtype=args.dtype)
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     log(f"[bench] {w} on {props.name} ({getattr(props, 'gcnArchName', '?')}, "
@@ -421,7 +429,7 @@ def main() -> int:
     dom = max(kernels, key=lambda kn: kern_ms[kn])
     wk = work[dom]
     ai = wk["flops"] / wk["bytes"]
-    if w.dtype == "bf16":
+    if w.dtype in ("bf16", "fp16"):
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         mfma_bound = ai >= ridge
         peak_c, bound_c = MFMA_BF16_PEAK_TFLOPS, "mfma"

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 MASK_CODES = {"none": 0, "causal": 1, "sliding": 2, "block": 3}
-DTYPE_CODES = {torch.bfloat16: 0, torch.float32: 1}
+DTYPE_CODES = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
 
 _lib = None
 
@@ -138,7 +138,7 @@ def _geometry(q, k, v, mask=None, window=None):
     if (Bq, Hq, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share dtype bfloat16 or float32")
+        raise ValueError("q, k, v must share dtype bfloat16, float16 or float32")
     if q.dim() == 5:
         if q.shape[1] != k.shape[1]:
             raise ValueError("q and k must have the same number of windows")

@@ -25,14 +25,17 @@ constexpr int64_t kMaxGrid = INT_MAX;           // 1-D grid of workgroups
 
 bool supported_d(int64_t d) { return d == 64 || d == 96 || d == 128; }
 
-size_t elem_size(int dtype) { return dtype == ATTN_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == ATTN_FP32 ? 4 : 2; }
+
+// bf16 and fp16 share the 16-bit kernels (MFMA with fp32 accumulation)
+bool is16(int dtype) { return dtype == ATTN_BF16 || dtype == ATTN_FP16; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Common checks of sizes, dtype, d, mask and window.
 int check_geometry(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                    float scale, int mask, int64_t window) {
-  if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+  if (!is16(dtype) && dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
   if (Nq > kMaxSeq || Nk > kMaxSeq || B * H > kMaxGrid) return ATTN_ERR_INVALID_ARG;
@@ -94,7 +97,7 @@ attn::MaskGeom make_geom(int mask, int64_t Nq, int64_t Nk, int64_t window) {
 // The dK/dV pass keeps dS for the dQ pass (bf16, general kernels, d = 128):
 // B * H * ds_blocks() blocks of 32 x 32 bf16 after the row sums.
 bool ds_applies(int dtype, int64_t d, const attn::MaskGeom& g) {
-  return dtype == ATTN_BF16 && d == 128 && !g.local64();
+  return is16(dtype) && d == 128 && !g.local64();
 }
 
 size_t ds_ws_size(int64_t B, int64_t H, int64_t Nq, const attn::MaskGeom& g) {
@@ -414,7 +417,7 @@ size_t attn_bwd_workspace_size_ds(int dtype, int64_t B, int64_t H, int64_t Nq, i
 int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int mask,
                    int64_t window) {
   if (check_geometry(dtype, B, H, Nq, Nk, d, 1.0f, mask, window) != ATTN_OK) return 0;
-  if (dtype != ATTN_BF16) return 0;
+  if (!is16(dtype)) return 0;
   return make_geom(mask, Nq, Nk, window).local64() ? 1 : 0;
 }
 
@@ -449,8 +452,8 @@ int attn_fwd_strided(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, in
   a.rv = rowmap(layouts->v, Nk, tk);
   a.ro = rowmap(layouts->o, Nq, tq);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int err = dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a, (int)d, s)
-                                     : attn::launch_fwd_fp32(a, (int)d, s);
+  const int err = is16(dtype) ? attn::launch_fwd_16(a, dtype == ATTN_FP16, (int)d, s)
+                              : attn::launch_fwd_fp32(a, (int)d, s);
   return err ? ATTN_ERR_LAUNCH : ATTN_OK;
 }
 
@@ -512,8 +515,8 @@ int attn_bwd_strided(int passes, int dtype, int64_t B, int64_t H, int64_t Nq, in
   a.rdk = rowmap(layouts->dk, Nk, tk);
   a.rdv = rowmap(layouts->dv, Nk, tk);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int err = dtype == ATTN_BF16 ? attn::launch_bwd_bf16(a, (int)d, s, passes)
-                                     : attn::launch_bwd_fp32(a, (int)d, s, passes);
+  const int err = is16(dtype) ? attn::launch_bwd_16(a, dtype == ATTN_FP16, (int)d, s, passes)
+                              : attn::launch_bwd_fp32(a, (int)d, s, passes);
   return err ? ATTN_ERR_LAUNCH : ATTN_OK;
 }
 

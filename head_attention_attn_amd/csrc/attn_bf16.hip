@@ -35,8 +35,9 @@ namespace {
 
 // ------------------------------------------------------------------ forward
 
-template <int D, int NW, int MODE, bool SR>
+template <typename E, int D, int NW, int MODE, bool SR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdArgs a, int nqt) {
+  using V8 = typename E::v8;
   static_assert(NW == 4, "O staging assumes 4 waves (two 64-row tiles)");
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, TE = tile_elems<BN, D>();
   constexpr int KC = D / 16, DB = D / 32;
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
     dma_tile<BN, D, NT, SR>(sV0, V, a.rv, t0, a.nk, tid);
   }
-  bf16x8 qop[KC];
-  load_operand_rows<D>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
+  V8 qop[KC];
+  load_operand_rows<D, E>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
 
   float m = -INFINITY, l = 0.f;
   f32x16 oacc[DB];
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       s[mb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        s[mb] = mfma32(lds_row8<D>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
+        s[mb] = mfma32<E>(lds_row8<D, E>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -129,10 +130,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c) {
-      const bf16x8 pop = acc_chunk(s[c >> 1], c & 1);
+      const V8 pop = acc_chunk<E>(s[c >> 1], c & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        oacc[db] = mfma32(lds_tr8<D>(v_l, 16 * c, 32 * db, lane), pop, oacc[db]);
+        oacc[db] = mfma32<E>(lds_tr8<D, E>(v_l, 16 * c, 32 * db, lane), pop, oacc[db]);
     }
   };
 
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // barrier, and with no visible key no tile was loaded): O rows go through
   // sK0 (waves 0, 1) and sV0 (waves 2, 3) for whole-row 16-byte stores
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  acc_to_lds<D>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), oacc, inv, gq);
+  acc_to_lds<D, E>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), oacc, inv, gq);
   if (qvalid && gq == 0)
     a.lse[(int64_t)bh * a.nq + myq] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
   __syncthreads();
@@ -170,8 +171,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // ------------------------------------------------------- backward: row sums
 
 // 16 rows of one (b, h) slice per workgroup, 16 lanes per row
-template <int D, bool SR>
+template <typename E, int D, bool SR>
 __global__ __launch_bounds__(256) void dsum_bf16_kernel(BwdArgs a, int nblk) {
+  using V8 = typename E::v8;
   const int bh = blockIdx.x / nblk;
   const int row = (blockIdx.x % nblk) * 16 + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
@@ -181,8 +183,8 @@ __global__ __launch_bounds__(256) void dsum_bf16_kernel(BwdArgs a, int nblk) {
         (const uint16_t*)a.o + rslice<SR, D>(a.ro, bh, a.H, a.nq) + rrow<SR, D>(a.ro, row);
     const uint16_t* g =
         (const uint16_t*)a.dout + rslice<SR, D>(a.rdo, bh, a.H, a.nq) + rrow<SR, D>(a.rdo, row);
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + 8 * li);
-    const bf16x8 y = *reinterpret_cast<const bf16x8*>(g + 8 * li);
+    const V8 x = *reinterpret_cast<const V8*>(o + 8 * li);
+    const V8 y = *reinterpret_cast<const V8*>(g + 8 * li);
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc += (float)x[s] * (float)y[s];
   }
@@ -208,8 +210,9 @@ struct DkdvShape {
   static constexpr int WPE = D == 128 ? 1 : 2;
 };
 
-template <int D, int NW, int MODE, bool SR>
+template <typename E, int D, int NW, int MODE, bool SR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvShape<D>::WPE))) void dkdv_bf16_kernel(BwdArgs a, int nkt) {
+  using V8 = typename E::v8;
   static_assert(NW == 4, "dK/dV staging assumes 4 waves");
   constexpr int KB = DkdvShape<D>::KB, BQ = DkdvShape<D>::BQ;
   constexpr int NT = NW * 64, BK = 32 * KB * NW, TE = tile_elems<BQ, D>();
@@ -256,14 +259,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   };
   if (lo < hi) load(sQ0, sG0, sS0, t0);
 
-  bf16x8 kop[KB][KC], vop[KB][KC];
+  V8 kop[KB][KC], vop[KB][KC];
   int clo[KB], chi[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int myk = wk0 + 32 * kb + (lane & 31);
     const bool kvalid = myk < a.nk;
-    load_operand_rows<D>(kop[kb], K + rrow<SR, D>(a.rk, myk), kvalid, gq);
-    load_operand_rows<D>(vop[kb], V + rrow<SR, D>(a.rv, myk), kvalid, gq);
+    load_operand_rows<D, E>(kop[kb], K + rrow<SR, D>(a.rk, myk), kvalid, gq);
+    load_operand_rows<D, E>(vop[kb], V + rrow<SR, D>(a.rv, myk), kvalid, gq);
     clo[kb] = kvalid ? mg.col_lo(myk) : 0;
     chi[kb] = kvalid ? mg.col_hi(myk) : 0;
   }
@@ -293,15 +296,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
       }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8 qr = lds_row8<D>(q_l, 32 * h, lane & 31, kc, gq);
-        const bf16x8 gr = lds_row8<D>(g_l, 32 * h, lane & 31, kc, gq);
+        const V8 qr = lds_row8<D, E>(q_l, 32 * h, lane & 31, kc, gq);
+        const V8 gr = lds_row8<D, E>(g_l, 32 * h, lane & 31, kc, gq);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          s[kb] = mfma32(qr, kop[kb][kc], s[kb]);
-          dp[kb] = mfma32(gr, vop[kb][kc], dp[kb]);
+          s[kb] = mfma32<E>(qr, kop[kb][kc], s[kb]);
+          dp[kb] = mfma32<E>(gr, vop[kb][kc], dp[kb]);
         }
       }
-      bf16x8 pop[KB][2], dsop[KB][2];
+      V8 pop[KB][2], dsop[KB][2];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int bk0 = wk0 + 32 * kb;
@@ -322,20 +325,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          pop[kb][c] = acc_chunk(s[kb], c);
-          dsop[kb][c] = acc_chunk(dp[kb], c);
+          pop[kb][c] = acc_chunk<E>(s[kb], c);
+          dsop[kb][c] = acc_chunk<E>(dp[kb], c);
         }
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 gt = lds_tr8<D>(g_l, 32 * h + 16 * c, 32 * db, lane);
-          const bf16x8 qt = lds_tr8<D>(q_l, 32 * h + 16 * c, 32 * db, lane);
+          const V8 gt = lds_tr8<D, E>(g_l, 32 * h + 16 * c, 32 * db, lane);
+          const V8 qt = lds_tr8<D, E>(q_l, 32 * h + 16 * c, 32 * db, lane);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            dvacc[kb][db] = mfma32(gt, pop[kb][c], dvacc[kb][db]);
-            dkacc[kb][db] = mfma32(qt, dsop[kb][c], dkacc[kb][db]);
+            dvacc[kb][db] = mfma32<E>(gt, pop[kb][c], dvacc[kb][db]);
+            dkacc[kb][db] = mfma32<E>(qt, dsop[kb][c], dkacc[kb][db]);
           }
         }
     }
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
     uint16_t* mine = bufs(wave / WPB);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      acc_to_lds<D>(mine, (wave % WPB) * WR + 32 * kb + (lane & 31), pass ? dvacc[kb] : dkacc[kb],
+      acc_to_lds<D, E>(mine, (wave % WPB) * WR + 32 * kb + (lane & 31), pass ? dvacc[kb] : dkacc[kb],
                     pass ? 1.f : a.scale, gq);
     __syncthreads();
     uint16_t* dst = pass ? dV : dK;
@@ -393,8 +396,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
 // a score wave's softmax arithmetic overlaps its partner's MFMAs.  Q / dO
 // tiles cycle through three named buffers (one being loaded, one read by the
 // score waves, one by the accumulate waves), P / dS through three more.
-template <int D, int MODE, bool SR>
+template <typename E, int D, int MODE, bool SR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void dkdv_pp_kernel(BwdArgs a, int nkt) {
+  using V8 = typename E::v8;
+  using V4 = typename E::v4;
   constexpr int NT = 512, BK = 128, BQ = 32, TE = tile_elems<BQ, D>();
   constexpr int KC = D / 16, DB = D / 32, PE = 4 * 2 * 64 * 8;  // 4 blocks x 2 chunks x 64 lanes x 16 B
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TE];
@@ -479,9 +484,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
     const int myk = wk0 + (lane & 31);
     const bool kvalid = myk < a.nk;
-    bf16x8 kop[KC], vop[KC];
-    load_operand_rows<D>(kop, K + rrow<SR, D>(a.rk, myk), kvalid, gq);
-    load_operand_rows<D>(vop, V + rrow<SR, D>(a.rv, myk), kvalid, gq);
+    V8 kop[KC], vop[KC];
+    load_operand_rows<D, E>(kop, K + rrow<SR, D>(a.rk, myk), kvalid, gq);
+    load_operand_rows<D, E>(vop, V + rrow<SR, D>(a.rv, myk), kvalid, gq);
     const int clo = kvalid ? mg.col_lo(myk) : 0;
     const int chi = kvalid ? mg.col_hi(myk) : 0;
     const float sl2 = a.scale * kLog2e;
@@ -494,8 +499,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        s = mfma32(lds_row8<D>(q_l, 0, lane & 31, kc, gq), kop[kc], s);
-        dp = mfma32(lds_row8<D>(g_l, 0, lane & 31, kc, gq), vop[kc], dp);
+        s = mfma32<E>(lds_row8<D, E>(q_l, 0, lane & 31, kc, gq), kop[kc], s);
+        dp = mfma32<E>(lds_row8<D, E>(g_l, 0, lane & 31, kc, gq), vop[kc], dp);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -515,12 +520,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       uint16_t* dt = d_l + kb * 1024;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        *reinterpret_cast<bf16x8*>(p_l + hoff + c * 512) = acc_chunk(s, c);
-        const bf16x8 v = acc_chunk(dp, c);
-        *reinterpret_cast<bf16x4*>(dt + (lane & 31) * 32 + 16 * c + 4 * gq) =
-            bf16x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<bf16x4*>(dt + (lane & 31) * 32 + 16 * c + 8 + 4 * gq) =
-            bf16x4{v[4], v[5], v[6], v[7]};
+        *reinterpret_cast<V8*>(p_l + hoff + c * 512) = acc_chunk<E>(s, c);
+        const V8 v = acc_chunk<E>(dp, c);
+        *reinterpret_cast<V4*>(dt + (lane & 31) * 32 + 16 * c + 4 * gq) = V4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<V4*>(dt + (lane & 31) * 32 + 16 * c + 8 + 4 * gq) =
+            V4{v[4], v[5], v[6], v[7]};
       }
     };
 
@@ -576,20 +580,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
         uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
-          *reinterpret_cast<bf16x8*>(blk + (cc * 64 + lane) * 8) =
-              lds_tr8_plain(d_l + kb * 1024, 32, 16 * cc, 0, lane);
+          *reinterpret_cast<V8*>(blk + (cc * 64 + lane) * 8) =
+              lds_tr8_plain<E>(d_l + kb * 1024, 32, 16 * cc, 0, lane);
       }
       const uint16_t* dt = d_l + kb * 1024 + (lane & 31) * 32;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 pop = *reinterpret_cast<const bf16x8*>(p_l + hoff + c * 512);
-        const bf16x4 d0 = *reinterpret_cast<const bf16x4*>(dt + 16 * c + 4 * gq);
-        const bf16x4 d1 = *reinterpret_cast<const bf16x4*>(dt + 16 * c + 8 + 4 * gq);
-        const bf16x8 dsop = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        const V8 pop = *reinterpret_cast<const V8*>(p_l + hoff + c * 512);
+        const V4 d0 = *reinterpret_cast<const V4*>(dt + 16 * c + 4 * gq);
+        const V4 d1 = *reinterpret_cast<const V4*>(dt + 16 * c + 8 + 4 * gq);
+        const V8 dsop = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dvacc[db] = mfma32(lds_tr8<D>(g_l, 16 * c, 32 * db, lane), pop, dvacc[db]);
-          dkacc[db] = mfma32(lds_tr8<D>(q_l, 16 * c, 32 * db, lane), dsop, dkacc[db]);
+          dvacc[db] = mfma32<E>(lds_tr8<D, E>(g_l, 16 * c, 32 * db, lane), pop, dvacc[db]);
+          dkacc[db] = mfma32<E>(lds_tr8<D, E>(q_l, 16 * c, 32 * db, lane), dsop, dkacc[db]);
         }
       }
     };
@@ -612,7 +616,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     // dK, then dV: 32 rows per wave through sQ0 / sG0 / sQ1 / sG1
     uint16_t* mine = kb == 0 ? sQ0 : kb == 1 ? sG0 : kb == 2 ? sQ1 : sG1;
-    acc_to_lds<D>(mine, lane & 31, dkacc, a.scale, gq);
+    acc_to_lds<D, E>(mine, lane & 31, dkacc, a.scale, gq);
     __syncthreads();
     uint16_t* dK = (uint16_t*)a.dk + rslice<SR, D>(a.rdk, bh, a.H, a.nk);
     store_tile<32, D, 256, SR>(dK, a.rdk, k0, a.nk, sQ0, tid - 256);
@@ -620,7 +624,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 64, a.nk, sQ1, tid - 256);
     store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 96, a.nk, sG1, tid - 256);
     __syncthreads();
-    acc_to_lds<D>(mine, lane & 31, dvacc, 1.f, gq);
+    acc_to_lds<D, E>(mine, lane & 31, dvacc, 1.f, gq);
     __syncthreads();
     uint16_t* dV = (uint16_t*)a.dv + rslice<SR, D>(a.rdv, bh, a.H, a.nk);
     store_tile<32, D, 256, SR>(dV, a.rdv, k0, a.nk, sQ0, tid - 256);
@@ -635,8 +639,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 // LDS (transpose reads give K^T), each wave's dS operands (16 bytes per lane
 // per 16-key chunk, stored by the dK/dV pass in exactly this register order)
 // loaded from the workspace one key tile ahead.
-template <int D, int MODE, bool SR>
+template <typename E, int D, int MODE, bool SR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dq_ds_kernel(BwdArgs a, int nqt) {
+  using V8 = typename E::v8;
   constexpr int NT = 256, BM = 128, BN = 128, TE = tile_elems<BN, D>();
   constexpr int DB = D / 32, NKB = BN / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK0[TE];
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   int64_t cur = lo < hi ? ds_offset(mg, kbn, lane) : 0;
   // operands of the 4 key blocks of one tile; bit kb of the mask: block kb
   // has this wave's query block
-  auto fetch = [&](bf16x8 (&op)[NKB][2], unsigned& valid) {
+  auto fetch = [&](V8 (&op)[NKB][2], unsigned& valid) {
     valid = 0;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -673,7 +678,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         const uint16_t* blk = DS + (cur + (jq - jlo)) * kDsBlockElems;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
-          op[kb][cc] = *reinterpret_cast<const bf16x8*>(blk + (cc * 64 + lane) * 8);
+          op[kb][cc] = *reinterpret_cast<const V8*>(blk + (cc * 64 + lane) * 8);
         valid |= 1u << kb;
       }
       cur += cnt;
@@ -684,7 +689,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   f32x16 dqacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
-  auto tile = [&](const uint16_t* k_l, const bf16x8 (&op)[NKB][2], unsigned valid) {
+  auto tile = [&](const uint16_t* k_l, const V8 (&op)[NKB][2], unsigned valid) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if (!(valid & (1u << kb))) continue;
@@ -692,12 +697,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          dqacc[db] = mfma32(lds_tr8<D>(k_l, 32 * kb + 16 * cc, 32 * db, lane), op[kb][cc], dqacc[db]);
+          dqacc[db] = mfma32<E>(lds_tr8<D, E>(k_l, 32 * kb + 16 * cc, 32 * db, lane), op[kb][cc], dqacc[db]);
     }
   };
 
   if (lo < hi) {
-    bf16x8 opA[NKB][2], opB[NKB][2];
+    V8 opA[NKB][2], opB[NKB][2];
     unsigned vA = 0, vB = 0;
     dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
     fetch(opA, vA);
@@ -718,7 +723,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       __syncthreads();
     }
   }
-  acc_to_lds<D>(sK0, 32 * wave + (lane & 31), dqacc, a.scale, gq);
+  acc_to_lds<D, E>(sK0, 32 * wave + (lane & 31), dqacc, a.scale, gq);
   __syncthreads();
   store_tile<BM, D, NT, SR>((uint16_t*)a.dq + rslice<SR, D>(a.rdq, bh, a.H, a.nq), a.rdq, i0, a.nq,
                             sK0, tid);
@@ -726,8 +731,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
 // ------------------------------------------------------------ backward: dQ
 
-template <int D, int NW, int MODE, bool SR>
+template <typename E, int D, int NW, int MODE, bool SR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void dq_bf16_kernel(BwdArgs a, int nqt) {
+  using V8 = typename E::v8;
   static_assert(NW == 4, "dQ staging assumes 4 waves (two 64-row tiles)");
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, TE = tile_elems<BN, D>();
   constexpr int KC = D / 16, DB = D / 32;
@@ -766,9 +772,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
     dma_tile<BN, D, NT, SR>(sV0, V, a.rv, t0, a.nk, tid);
   }
-  bf16x8 qop[KC], dop[KC];
-  load_operand_rows<D>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
-  load_operand_rows<D>(dop, dO + rrow<SR, D>(a.rdo, myq), qvalid, gq);
+  V8 qop[KC], dop[KC];
+  load_operand_rows<D, E>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
+  load_operand_rows<D, E>(dop, dO + rrow<SR, D>(a.rdo, myq), qvalid, gq);
   const float lse2 = qvalid ? a.lse[(int64_t)bh * a.nq + myq] * kLog2e : 0.f;
   const float dsv = qvalid ? a.dsum[(int64_t)bh * a.nq + myq] : 0.f;
 
@@ -781,14 +787,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto tile = [&](const uint16_t* k_l, const uint16_t* v_l, int j0) {
     if (!(wlo < whi && j0 < whi && j0 + BN > wlo)) return;
     const bool full = mg.tile_full(wa, wb, j0, j0 + BN);
-    bf16x8 dsop[BN / 16];
+    V8 dsop[BN / 16];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        s = mfma32(lds_row8<D>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], s);
-        dp = mfma32(lds_row8<D>(v_l, mb * 32, lane & 31, kc, gq), dop[kc], dp);
+        s = mfma32<E>(lds_row8<D, E>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], s);
+        dp = mfma32<E>(lds_row8<D, E>(v_l, mb * 32, lane & 31, kc, gq), dop[kc], dp);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -800,14 +806,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const float p = vis ? fast_exp2(s[e] * sl2 - lse2) : 0.f;
         s[e] = p * (dp[e] - dsv);
       }
-      dsop[2 * mb] = acc_chunk(s, 0);
-      dsop[2 * mb + 1] = acc_chunk(s, 1);
+      dsop[2 * mb] = acc_chunk<E>(s, 0);
+      dsop[2 * mb + 1] = acc_chunk<E>(s, 1);
     }
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        dqacc[db] = mfma32(lds_tr8<D>(k_l, 16 * c, 32 * db, lane), dsop[c], dqacc[db]);
+        dqacc[db] = mfma32<E>(lds_tr8<D, E>(k_l, 16 * c, 32 * db, lane), dsop[c], dqacc[db]);
   };
 
   if (lo < hi) {
@@ -828,42 +834,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       __syncthreads();
     }
   }
-  acc_to_lds<D>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), dqacc, a.scale, gq);
+  acc_to_lds<D, E>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), dqacc, a.scale, gq);
   __syncthreads();
   uint16_t* dQ = (uint16_t*)a.dq + rslice<SR, D>(a.rdq, bh, a.H, a.nq);
   store_tile<64, D, NT, SR>(dQ, a.rdq, i0, a.nq, sK0, tid);
   store_tile<64, D, NT, SR>(dQ, a.rdq, i0 + 64, a.nq, sV0, tid);
 }
 
-template <int D, int MODE, bool SR>
+template <typename E, int D, int MODE, bool SR>
 int launch_fwd_dm(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = 4, BM = 32 * NW;
   const int nqt = (a.nq + BM - 1) / BM;
   const int64_t grid = (int64_t)nqt * a.B * a.H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kAnyMask, SR>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<E, D, NW, kAnyMask, SR>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      s, a, nqt);
   return (int)hipGetLastError();
 }
 
-template <int D, int MODE, bool SR>
+template <typename E, int D, int MODE, bool SR>
 int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
   constexpr int NW = 4;
   int err = 0;
   if (passes & kPassRowSum) {
     const int nblk = (a.nq + 15) / 16;
-    hipLaunchKernelGGL((dsum_bf16_kernel<D, SR>), dim3((unsigned)((int64_t)nblk * a.B * a.H)),
+    hipLaunchKernelGGL((dsum_bf16_kernel<E, D, SR>), dim3((unsigned)((int64_t)nblk * a.B * a.H)),
                        dim3(256), 0, s, a, nblk);
     if ((err = (int)hipGetLastError())) return err;
   }
   if (passes & kPassDKDV) {
     if constexpr (D == 128) {
       const int nkt = (a.nk + 127) / 128;
-      hipLaunchKernelGGL((dkdv_pp_kernel<D, kAnyMask, SR>),
+      hipLaunchKernelGGL((dkdv_pp_kernel<E, D, kAnyMask, SR>),
                          dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(512), 0, s, a, nkt);
     } else {
       constexpr int BK = 32 * DkdvShape<D>::KB * NW;
       const int nkt = (a.nk + BK - 1) / BK;
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, kAnyMask, SR>),
+      hipLaunchKernelGGL((dkdv_bf16_kernel<E, D, NW, kAnyMask, SR>),
                          dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(NW * 64), 0, s, a, nkt);
     }
     if ((err = (int)hipGetLastError())) return err;
@@ -873,23 +879,23 @@ int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
     bool done = false;
     if constexpr (D == 128) {
       if (a.ds) {
-        hipLaunchKernelGGL((dq_ds_kernel<D, MODE, SR>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
+        hipLaunchKernelGGL((dq_ds_kernel<E, D, MODE, SR>), dim3((unsigned)((int64_t)nqt * a.B * a.H)),
                            dim3(256), 0, s, a, nqt);
         done = true;
       }
     }
     if (!done)
-      hipLaunchKernelGGL((dq_bf16_kernel<D, NW, MODE, SR>),
+      hipLaunchKernelGGL((dq_bf16_kernel<E, D, NW, MODE, SR>),
                          dim3((unsigned)((int64_t)nqt * a.B * a.H)), dim3(NW * 64), 0, s, a, nqt);
     if ((err = (int)hipGetLastError())) return err;
   }
   return 0;
 }
 
-template <int D>
+template <typename E, int D>
 int launch_fwd_d(const FwdArgs& a, hipStream_t s) {
-  if (rows_plain(a, D)) return launch_fwd_dm<D, kAnyMask, false>(a, s);
-  return launch_fwd_dm<D, kAnyMask, true>(a, s);
+  if (rows_plain(a, D)) return launch_fwd_dm<E, D, kAnyMask, false>(a, s);
+  return launch_fwd_dm<E, D, kAnyMask, true>(a, s);
 }
 
 // The dQ kernel is instantiated per mask mode (measured 16% faster on the
@@ -897,47 +903,57 @@ int launch_fwd_d(const FwdArgs& a, hipStream_t s) {
 // and dK/dV kernels read the mode at run time (their per-mode instances
 // measured 3-4% slower on the causal workload).  Every kernel comes in a
 // contiguous-rows and a strided-rows instance.
-template <int D, bool SR>
+template <typename E, int D, bool SR>
 int launch_bwd_ds(const BwdArgs& a, hipStream_t s, int passes) {
   switch (a.mg.mode) {
-    case kNone: return launch_bwd_dm<D, kNone, SR>(a, s, passes);
-    case kCausal: return launch_bwd_dm<D, kCausal, SR>(a, s, passes);
-    case kSliding: return launch_bwd_dm<D, kSliding, SR>(a, s, passes);
-    case kBlock: return launch_bwd_dm<D, kBlock, SR>(a, s, passes);
+    case kNone: return launch_bwd_dm<E, D, kNone, SR>(a, s, passes);
+    case kCausal: return launch_bwd_dm<E, D, kCausal, SR>(a, s, passes);
+    case kSliding: return launch_bwd_dm<E, D, kSliding, SR>(a, s, passes);
+    case kBlock: return launch_bwd_dm<E, D, kBlock, SR>(a, s, passes);
   }
   return (int)hipErrorInvalidValue;
 }
 
-template <int D>
+template <typename E, int D>
 int launch_bwd_d(const BwdArgs& a, hipStream_t s, int passes) {
-  return rows_plain(a, D) ? launch_bwd_ds<D, false>(a, s, passes)
-                          : launch_bwd_ds<D, true>(a, s, passes);
+  return rows_plain(a, D) ? launch_bwd_ds<E, D, false>(a, s, passes)
+                          : launch_bwd_ds<E, D, true>(a, s, passes);
+}
+
+template <typename E>
+int launch_fwd_e(const FwdArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_fwd_d<E, 64>(a, s);
+    case 96: return launch_fwd_d<E, 96>(a, s);
+    case 128: return launch_fwd_d<E, 128>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <typename E>
+int launch_bwd_e(const BwdArgs& a, int d, hipStream_t s, int passes) {
+  switch (d) {
+    case 64: return launch_bwd_d<E, 64>(a, s, passes);
+    case 96: return launch_bwd_d<E, 96>(a, s, passes);
+    case 128: return launch_bwd_d<E, 128>(a, s, passes);
+  }
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
-  if (a.mg.local64()) return launch_fwd_bf16_local(a, d, s);
-  switch (d) {
-    case 64: return launch_fwd_d<64>(a, s);
-    case 96: return launch_fwd_d<96>(a, s);
-    case 128: return launch_fwd_d<128>(a, s);
-  }
-  return (int)hipErrorInvalidValue;
+int launch_fwd_16(const FwdArgs& a, bool f16, int d, hipStream_t s) {
+  if (a.mg.local64()) return launch_fwd_16_local(a, f16, d, s);
+  return f16 ? launch_fwd_e<F16>(a, d, s) : launch_fwd_e<Bf16>(a, d, s);
 }
 
-int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s, int passes) {
+int launch_bwd_16(const BwdArgs& a, bool f16, int d, hipStream_t s, int passes) {
   if (a.mg.local64()) {
     // one fused kernel writes dQ, dK and dV; it takes no partial pass set
     if (passes != kPassAll) return (int)hipErrorInvalidValue;
-    return launch_bwd_bf16_local(a, d, s);
+    return launch_bwd_16_local(a, f16, d, s);
   }
-  switch (d) {
-    case 64: return launch_bwd_d<64>(a, s, passes);
-    case 96: return launch_bwd_d<96>(a, s, passes);
-    case 128: return launch_bwd_d<128>(a, s, passes);
-  }
-  return (int)hipErrorInvalidValue;
+  return f16 ? launch_bwd_e<F16>(a, d, s, passes) : launch_bwd_e<Bf16>(a, d, s, passes);
 }
 
 }  // namespace attn

@@ -62,8 +62,9 @@ __device__ __forceinline__ LocalTile local_tile(int tile, int nq, int lw, int lq
 // ------------------------------------------------------------------ forward
 
 // QR: query buffer rows (32 when QT <= 32, else 64); one wave per 32 rows
-template <int D, int QR, bool SR>
+template <typename E, int D, int QR, bool SR>
 __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
+  using V8 = typename E::v8;
   constexpr int NT = 2 * QR, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[TE];
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int myr = wave * 32 + (lane & 31);  // this lane's query row in the tile
   const int myq = lt.tq0 + myr;
   const bool qvalid = lt.real(myr);
-  bf16x8 qop[KC];
-  load_operand_rows<D>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
+  V8 qop[KC];
+  load_operand_rows<D, E>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
   __syncthreads();
 
   f32x16 s[2];
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
     s[mb] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      s[mb] = mfma32(lds_row8<D>(sK, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
+      s[mb] = mfma32<E>(lds_row8<D, E>(sK, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
   }
   // one 64-key window of 64 rows, whole: nothing to mask
   const bool full = lw == 6 && lq == 6 && tk0 + kTile <= a.nk;
@@ -130,15 +131,15 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 #pragma unroll
   for (int c = 0; c < kTile / 16; ++c) {
-    const bf16x8 pop = acc_chunk(s[c >> 1], c & 1);
+    const V8 pop = acc_chunk<E>(s[c >> 1], c & 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      oacc[db] = mfma32(lds_tr8<D>(sV, 16 * c, 32 * db, lane), pop, oacc[db]);
+      oacc[db] = mfma32<E>(lds_tr8<D, E>(sV, 16 * c, 32 * db, lane), pop, oacc[db]);
   }
   // O rows through LDS (sK is free once every wave is past its products) so
   // that the global stores are whole rows, 16 bytes per lane
   __syncthreads();
-  acc_to_lds<D>(sK, myr, oacc, qvalid ? 1.f / l : 0.f, gq);
+  acc_to_lds<D, E>(sK, myr, oacc, qvalid ? 1.f / l : 0.f, gq);
   if (qvalid && gq == 0) a.lse[(int64_t)bh * a.nq + myq] = (mb2 + log2f(l)) * kLn2;
   __syncthreads();
   uint16_t* O = (uint16_t*)a.o + rslice<SR, D>(a.ro, bh, a.H, a.nq);
@@ -149,8 +150,9 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
 
 // QR: query buffer rows; waves 0-1 own the tile's keys, the QR / 32 waves
 // after them its query rows
-template <int D, int QR, bool SR>
+template <typename E, int D, int QR, bool SR>
 __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int ntile, int lw, int lq) {
+  using V8 = typename E::v8;
   constexpr int NT = 128 + 2 * QR, KE = tile_elems<kTile, D>(), QE = tile_elems<QR, D>();
   constexpr int KC = D / 16, DB = D / 32, QB = QR / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sQ[QE];
@@ -202,9 +204,9 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
       y[mb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        x[mb] = mfma32(lds_row8<D>(sK, 32 * mb, lane & 31, kc, gq), lds_row8<D>(sQ, 0, own, kc, gq),
+        x[mb] = mfma32<E>(lds_row8<D, E>(sK, 32 * mb, lane & 31, kc, gq), lds_row8<D, E>(sQ, 0, own, kc, gq),
                        x[mb]);
-        y[mb] = mfma32(lds_row8<D>(sV, 32 * mb, lane & 31, kc, gq), lds_row8<D>(sG, 0, own, kc, gq),
+        y[mb] = mfma32<E>(lds_row8<D, E>(sV, 32 * mb, lane & 31, kc, gq), lds_row8<D, E>(sG, 0, own, kc, gq),
                        y[mb]);
       }
     }
@@ -232,9 +234,9 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
       y[qt] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        x[qt] = mfma32(lds_row8<D>(sQ, 32 * qt, lane & 31, kc, gq), lds_row8<D>(sK, 0, own, kc, gq),
+        x[qt] = mfma32<E>(lds_row8<D, E>(sQ, 32 * qt, lane & 31, kc, gq), lds_row8<D, E>(sK, 0, own, kc, gq),
                        x[qt]);
-        y[qt] = mfma32(lds_row8<D>(sG, 32 * qt, lane & 31, kc, gq), lds_row8<D>(sV, 0, own, kc, gq),
+        y[qt] = mfma32<E>(lds_row8<D, E>(sG, 32 * qt, lane & 31, kc, gq), lds_row8<D, E>(sV, 0, own, kc, gq),
                        y[qt]);
       }
 #pragma unroll
@@ -250,10 +252,10 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
       // dV^T += dO^T P over this tile's 32 query rows
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 pop = acc_chunk(x[qt], c);
+        const V8 pop = acc_chunk<E>(x[qt], c);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc1[db] = mfma32(lds_tr8<D>(sG, 32 * qt + 16 * c, 32 * db, lane), pop, acc1[db]);
+          acc1[db] = mfma32<E>(lds_tr8<D, E>(sG, 32 * qt + 16 * c, 32 * db, lane), pop, acc1[db]);
       }
     }
   }
@@ -264,10 +266,10 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
     // dQ^T += K^T dS^T over the tile's 64 keys
 #pragma unroll
     for (int c = 0; c < kTile / 16; ++c) {
-      const bf16x8 dsop = acc_chunk(x[c >> 1], c & 1);
+      const V8 dsop = acc_chunk<E>(x[c >> 1], c & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        acc0[db] = mfma32(lds_tr8<D>(sK, 16 * c, 32 * db, lane), dsop, acc0[db]);
+        acc0[db] = mfma32<E>(lds_tr8<D, E>(sK, 16 * c, 32 * db, lane), dsop, acc0[db]);
     }
   } else {
 #pragma unroll
@@ -280,19 +282,19 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 dsop = acc_chunk(x[qt], c);
+        const V8 dsop = acc_chunk<E>(x[qt], c);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc0[db] = mfma32(lds_tr8<D>(sQ, 32 * qt + 16 * c, 32 * db, lane), dsop, acc0[db]);
+          acc0[db] = mfma32<E>(lds_tr8<D, E>(sQ, 32 * qt + 16 * c, 32 * db, lane), dsop, acc0[db]);
       }
     }
   }
   __syncthreads();
   if (dq_wave) {
-    acc_to_lds<D>(sQ, own, acc0, a.scale, gq);
+    acc_to_lds<D, E>(sQ, own, acc0, a.scale, gq);
   } else {
-    acc_to_lds<D>(sK, own, acc0, a.scale, gq);
-    acc_to_lds<D>(sV, own, acc1, 1.f, gq);
+    acc_to_lds<D, E>(sK, own, acc0, a.scale, gq);
+    acc_to_lds<D, E>(sV, own, acc1, 1.f, gq);
   }
   __syncthreads();
   store_tile<QR, D, NT, SR>((uint16_t*)a.dq + rslice<SR, D>(a.rdq, bh, a.H, a.nq), a.rdq, lt.tq0,
@@ -324,59 +326,69 @@ LocalLaunch local_launch(const MaskGeom& g) {
   return l;
 }
 
-template <int D, bool SR>
+template <typename E, int D, bool SR>
 int fwd_ds(const FwdArgs& a, hipStream_t s) {
   const LocalLaunch l = local_launch(a.mg);
   const dim3 grid((unsigned)((int64_t)l.ntile * a.B * a.H));
   if (l.wide)
-    hipLaunchKernelGGL((fwd_local_kernel<D, 64, SR>), grid, dim3(128), 0, s, a, l.ntile, l.lw,
+    hipLaunchKernelGGL((fwd_local_kernel<E, D, 64, SR>), grid, dim3(128), 0, s, a, l.ntile, l.lw,
                        l.lq);
   else
-    hipLaunchKernelGGL((fwd_local_kernel<D, 32, SR>), grid, dim3(64), 0, s, a, l.ntile, l.lw, l.lq);
+    hipLaunchKernelGGL((fwd_local_kernel<E, D, 32, SR>), grid, dim3(64), 0, s, a, l.ntile, l.lw, l.lq);
   return (int)hipGetLastError();
 }
 
-template <int D, bool SR>
+template <typename E, int D, bool SR>
 int bwd_ds(const BwdArgs& a, hipStream_t s) {
   const LocalLaunch l = local_launch(a.mg);
   const dim3 grid((unsigned)((int64_t)l.ntile * a.B * a.H));
   if (l.wide)
-    hipLaunchKernelGGL((bwd_local_kernel<D, 64, SR>), grid, dim3(256), 0, s, a, l.ntile, l.lw,
+    hipLaunchKernelGGL((bwd_local_kernel<E, D, 64, SR>), grid, dim3(256), 0, s, a, l.ntile, l.lw,
                        l.lq);
   else
-    hipLaunchKernelGGL((bwd_local_kernel<D, 32, SR>), grid, dim3(192), 0, s, a, l.ntile, l.lw,
+    hipLaunchKernelGGL((bwd_local_kernel<E, D, 32, SR>), grid, dim3(192), 0, s, a, l.ntile, l.lw,
                        l.lq);
   return (int)hipGetLastError();
 }
 
-template <int D>
+template <typename E, int D>
 int fwd_d(const FwdArgs& a, hipStream_t s) {
-  return rows_plain(a, D) ? fwd_ds<D, false>(a, s) : fwd_ds<D, true>(a, s);
+  return rows_plain(a, D) ? fwd_ds<E, D, false>(a, s) : fwd_ds<E, D, true>(a, s);
 }
 
-template <int D>
+template <typename E, int D>
 int bwd_d(const BwdArgs& a, hipStream_t s) {
-  return rows_plain(a, D) ? bwd_ds<D, false>(a, s) : bwd_ds<D, true>(a, s);
+  return rows_plain(a, D) ? bwd_ds<E, D, false>(a, s) : bwd_ds<E, D, true>(a, s);
+}
+
+template <typename E>
+int fwd_e(const FwdArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return fwd_d<E, 64>(a, s);
+    case 96: return fwd_d<E, 96>(a, s);
+    case 128: return fwd_d<E, 128>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <typename E>
+int bwd_e(const BwdArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return bwd_d<E, 64>(a, s);
+    case 96: return bwd_d<E, 96>(a, s);
+    case 128: return bwd_d<E, 128>(a, s);
+  }
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int launch_fwd_bf16_local(const FwdArgs& a, int d, hipStream_t s) {
-  switch (d) {
-    case 64: return fwd_d<64>(a, s);
-    case 96: return fwd_d<96>(a, s);
-    case 128: return fwd_d<128>(a, s);
-  }
-  return (int)hipErrorInvalidValue;
+int launch_fwd_16_local(const FwdArgs& a, bool f16, int d, hipStream_t s) {
+  return f16 ? fwd_e<F16>(a, d, s) : fwd_e<Bf16>(a, d, s);
 }
 
-int launch_bwd_bf16_local(const BwdArgs& a, int d, hipStream_t s) {
-  switch (d) {
-    case 64: return bwd_d<64>(a, s);
-    case 96: return bwd_d<96>(a, s);
-    case 128: return bwd_d<128>(a, s);
-  }
-  return (int)hipErrorInvalidValue;
+int launch_bwd_16_local(const BwdArgs& a, bool f16, int d, hipStream_t s) {
+  return f16 ? bwd_e<F16>(a, d, s) : bwd_e<Bf16>(a, d, s);
 }
 
 }  // namespace attn

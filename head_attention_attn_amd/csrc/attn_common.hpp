@@ -226,15 +226,16 @@ enum BwdPass : int { kPassRowSum = 1, kPassDKDV = 2, kPassDQ = 4, kPassAll = 7 }
 
 #if defined(__HIPCC__)
 namespace attn {
-// Launchers, one per dtype; each picks its kernel instantiation from (d, mask).
-// They return the hipError_t of the launch(es) as an int.  `passes` is a set
-// of backward pass bits (row sums, dK/dV, dQ), launched in that order.
-int launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
-int launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t s, int passes);
+// Launchers: the 16-bit ones (bf16, or fp16 with f16 set) and the fp32 ones;
+// each picks its kernel instantiation from (d, mask, layout).  They return the
+// hipError_t of the launch(es) as an int.  `passes` is a set of backward pass
+// bits (row sums, dK/dV, dQ), launched in that order.
+int launch_fwd_16(const FwdArgs& a, bool f16, int d, hipStream_t s);
+int launch_bwd_16(const BwdArgs& a, bool f16, int d, hipStream_t s, int passes);
 int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s);
-// single-tile bf16 kernels for MaskGeom::local64() (forward; fused backward)
-int launch_fwd_bf16_local(const FwdArgs& a, int d, hipStream_t s);
-int launch_bwd_bf16_local(const BwdArgs& a, int d, hipStream_t s);
+// single-tile 16-bit kernels for MaskGeom::local64() (forward; fused backward)
+int launch_fwd_16_local(const FwdArgs& a, bool f16, int d, hipStream_t s);
+int launch_bwd_16_local(const BwdArgs& a, bool f16, int d, hipStream_t s);
 int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s, int passes);
 }  // namespace attn
 #endif

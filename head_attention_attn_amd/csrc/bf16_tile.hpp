@@ -62,9 +62,10 @@ __host__ __device__ constexpr int tile_elems() {
 
 // MFMA operand from a row read: 8 consecutive bf16 of row r0 + rl at columns
 // 16 kc + 8 gq .. +7 (the contraction runs along the row); r0 % 16 == 0.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* tile, int r0, int rl, int kc, int gq) {
-  return *reinterpret_cast<const bf16x8*>(
+template <int D, typename E>
+__device__ __forceinline__ typename E::v8 lds_row8(const uint16_t* tile, int r0, int rl, int kc,
+                                                   int gq) {
+  return *reinterpret_cast<const typename E::v8*>(
       tile + toff2<D>(r0, rl, 32 * (kc >> 1), 16 * (kc & 1) + 8 * gq));
 }
 
@@ -74,8 +75,8 @@ __device__ __forceinline__ bf16x8 lds_row8(const uint16_t* tile, int r0, int rl,
 // rows r0 + 4g + e, slots 4..7 rows r0 + 8 + 4g + e (g = lane / 32,
 // e = 0..3) -- the row order of a 32x32 accumulator's 16-row chunk, so it
 // pairs with acc_chunk().  r0 % 16 == 0, c0 % 32 == 0.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_tr8(const uint16_t* tile, int r0, int c0, int lane) {
+template <int D, typename E>
+__device__ __forceinline__ typename E::v8 lds_tr8(const uint16_t* tile, int r0, int c0, int lane) {
   const int grp = lane >> 4, li = lane & 15;
   const int e = li >> 2, r = li & 3;
   const int g = grp >> 1, half = grp & 1;
@@ -85,7 +86,7 @@ __device__ __forceinline__ bf16x8 lds_tr8(const uint16_t* tile, int r0, int c0, 
       (lds_i16x4*)(tile + toff2<D>(r0, rl + 8, c0, cl)));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, w);
+  return __builtin_bit_cast(typename E::v8, w);
 }
 
 // Direct global -> LDS load of a ROWS x D bf16 tile (rows r0 .. r0+ROWS-1 of
@@ -129,7 +130,8 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, con
 // Transposed operand read of a plain row-major tile (row stride `stride`
 // elements, no swizzle): as lds_tr8 -- free index = column c0 + lane % 32,
 // contraction slots = rows r0 + 4g + e, r0 + 8 + 4g + e.
-__device__ __forceinline__ bf16x8 lds_tr8_plain(const uint16_t* tile, int stride, int r0, int c0,
+template <typename E>
+__device__ __forceinline__ typename E::v8 lds_tr8_plain(const uint16_t* tile, int stride, int r0, int c0,
                                                 int lane) {
   const int grp = lane >> 4, li = lane & 15;
   const int e = li >> 2, r = li & 3;
@@ -139,7 +141,7 @@ __device__ __forceinline__ bf16x8 lds_tr8_plain(const uint16_t* tile, int stride
   i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * stride));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, w);
+  return __builtin_bit_cast(typename E::v8, w);
 }
 
 // Index of key block kb's first dS block within its (b, h): the sum of
@@ -200,27 +202,26 @@ __device__ __forceinline__ void dma_rows_f32x2(float* lds, const float* a, const
 
 // Global -> register MFMA operand of one row (lane l: row l % 32, chunks
 // 2kc + l / 32); rows that are not valid read as zero.
-template <int D>
-__device__ __forceinline__ void load_operand_rows(bf16x8 (&op)[D / 16], const uint16_t* rowp,
+template <int D, typename E>
+__device__ __forceinline__ void load_operand_rows(typename E::v8 (&op)[D / 16], const uint16_t* rowp,
                                                   bool valid, int gq) {
 #pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
     if (valid) {
-      op[kc] = *reinterpret_cast<const bf16x8*>(rowp + 16 * kc + 8 * gq);
+      op[kc] = *reinterpret_cast<const typename E::v8*>(rowp + 16 * kc + 8 * gq);
     } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) op[kc][s] = (__bf16)0.0f;
+      op[kc] = typename E::v8{};
     }
   }
 }
 
 // Write a transposed accumulator set (accumulator rows = the d columns, this
 // lane's accumulator column = tile row `row`) into an LDS tile as
-// bf16, scaled by `mul`: element (row, 32*db + 8*i + 4*gq + j).  Output rows
+// E, scaled by `mul`: element (row, 32*db + 8*i + 4*gq + j).  Output rows
 // go through LDS so that store_tile() writes them with coalesced 16-byte
 // stores (storing one row per lane would scatter 8-byte pieces over 32 rows
 // per instruction).
-template <int D>
+template <int D, typename E>
 __device__ __forceinline__ void acc_to_lds(uint16_t* tile, int row, const f32x16 (&acc)[D / 32],
                                            float mul, int gq) {
 #pragma unroll
@@ -228,8 +229,8 @@ __device__ __forceinline__ void acc_to_lds(uint16_t* tile, int row, const f32x16
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint2*>(tile + toff2<D>(0, row, 32 * db, 8 * i + 4 * gq)) =
-          pack_bf16x4(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul,
-                      acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
+          pack4<E>(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul, acc[db][4 * i + 2] * mul,
+                   acc[db][4 * i + 3] * mul);
 }
 
 // LDS -> global copy of a ROWS x D tile to rows r0 .. of the n rows of a

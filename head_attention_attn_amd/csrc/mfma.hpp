@@ -1,6 +1,9 @@
-// mfma.hpp -- CDNA4 (gfx950) building blocks for the bf16 attention kernels.
+// mfma.hpp -- CDNA4 (gfx950) building blocks for the 16-bit (bf16 and fp16)
+// attention kernels.  The kernels are templates over an element type E, Bf16
+// or F16 below: storage is 16 bits either way, E supplies the MFMA operand
+// vector, the MFMA and the fp32 -> 16-bit conversion (round to nearest even).
 //
-// v_mfma_f32_32x32x16_bf16 lane layout (checked on gfx950 hardware):
+// v_mfma_f32_32x32x16_bf16 / _f16 lane layout (checked on gfx950 hardware):
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) + s, s = 0..7
 //   B (16 x 32): lane l holds col l%32, k = 8*(l/32) + s
 //   C (32 x 32): lane l holds col l%32, rows 8*i + 4*(l/32) + j in acc[4*i + j]
@@ -30,23 +33,47 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// element types of the 16-bit kernels
+struct Bf16 {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct F16 {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename E>
+__device__ __forceinline__ f32x16 mfma32(const typename E::v8& a, const typename E::v8& b,
+                                         const f32x16& c) {
+  return E::mfma(a, b, c);
 }
 
-// Accumulator entries 8c .. 8c+7 of a 32x32 tile, rounded to bf16: the rows
+// Accumulator entries 8c .. 8c+7 of a 32x32 tile, rounded to E: the rows
 // (8*(2c) + 4g + j, 8*(2c+1) + 4g + j) of chunk c in the order the transposed LDS read
 // uses, ready to be the other operand of a contraction over those rows.
-__device__ __forceinline__ bf16x8 acc_chunk(const f32x16& acc, int c) {
+template <typename E>
+__device__ __forceinline__ typename E::v8 acc_chunk(const f32x16& acc, int c) {
   f32x8 v;
   #pragma unroll
   for (int s = 0; s < 8; ++s) v[s] = acc[8 * c + s];
-  return __builtin_convertvector(v, bf16x8);
+  return __builtin_convertvector(v, typename E::v8);
 }
 
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+template <typename E>
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   f32x4 v = {a, b, c, d};
-  bf16x4 h = __builtin_convertvector(v, bf16x4);
+  typename E::v4 h = __builtin_convertvector(v, typename E::v4);
   return __builtin_bit_cast(uint2, h);
 }
 

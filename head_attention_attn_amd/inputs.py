@@ -4,7 +4,8 @@ This module holds no attention arithmetic: it only names the workloads and
 draws their inputs, so that the HIP library and the fp64 oracle are fed the
 very same values.  Recipe: one CPU ``torch.Generator`` seeded with ``seed``;
 Q, K, V, dO drawn in that order with ``torch.randn(shape, float32)``; for bf16
-workloads each tensor is then rounded to bfloat16 (round to nearest even).
+workloads each tensor is then rounded to bfloat16 (fp16 workloads: float16),
+round to nearest even.
 The oracle widens exactly these values to float64.
 
 Workloads (shapes after the pages' own models; the activations themselves
@@ -46,7 +47,7 @@ class Workload:
     Nq: int
     Nk: int
     d: int
-    dtype: str          # "bf16" or "fp32"
+    dtype: str          # "bf16", "fp16" or "fp32"
     mask: str           # "none" | "causal" | "sliding" | "block"
     window: int = 0
 
@@ -71,7 +72,7 @@ WORKLOADS = {
     )
 }
 
-TORCH_DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
+TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 def make_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str = "bf16",

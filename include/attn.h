@@ -34,7 +34,11 @@
  *     K, V, dK, dV : [B][H][Nk][d]
  *     lse          : [B][H][Nq]      natural-log logsumexp of the scaled,
  *                                    masked scores of each query row
- * Accumulation is always fp32.  bf16 outputs are rounded to nearest even.
+ * Element types: bf16 and fp16 (both on the MFMA units, products of 16-bit
+ * operands: P and dS are rounded to the input type before their products)
+ * and fp32 (vector ALUs).  Accumulation is always fp32.  16-bit outputs are
+ * rounded to nearest even.  fp16 inputs follow the hiera-optim test matrix
+ * (bf16 / fp16 / fp32; "hiera-optim 0.1.0", Tests).
  *
  * Visibility of key j to query i (absolute indices, top-left aligned):
  *     ATTN_MASK_NONE     every key
@@ -77,7 +81,7 @@
 extern "C" {
 #endif
 
-enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1 };
+enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1, ATTN_FP16 = 2 };
 
 enum attn_mask {
   ATTN_MASK_NONE = 0,
@@ -99,7 +103,8 @@ enum attn_status {
 
 /*
  * attn_fwd -- forward pass.
- *   dtype        ATTN_BF16 or ATTN_FP32 (element type of q, k, v, o)
+ *   dtype        ATTN_BF16, ATTN_FP16 or ATTN_FP32 (element type of q, k, v,
+ *                o and of every other tensor but lse)
  *   B, H         batch and head count (>= 1)
  *   Nq, Nk       query and key sequence lengths (>= 1)
  *   d            head dimension: 64, 96 or 128
@@ -126,13 +131,13 @@ ATTN_API size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
 
 /*
  * attn_bwd_workspace_size_ds -- bytes of workspace with which attn_bwd keeps
- * dS = P * (dP - D) (bf16) from its dK/dV pass for its dQ pass, so that the
+ * dS = P * (dP - D) (16-bit) from its dK/dV pass for its dQ pass, so that the
  * dQ pass is the plain product dQ = scale * dS K instead of recomputing S, P
  * and dP (a choice of this library: the pages' backward designs either
  * recompute or accumulate dQ with atomics).  The extra part holds one 32 x 32
- * bf16 block (2 KB) per key block x query block pair with a visible entry,
+ * 16-bit block (2 KB) per key block x query block pair with a visible entry,
  * per (b, h): about 2 bytes per visible (query, key) pair, e.g. 1.35 GB for
- * causal B=1, H=20, N=8192.  It applies to bf16, d = 128, and every mask
+ * causal B=1, H=20, N=8192.  It applies to bf16 and fp16, d = 128, and every mask
  * except the block-local one of attn_bwd_fused(); elsewhere, and for any
  * workspace smaller than this, attn_bwd recomputes and the value returned is
  * attn_bwd_workspace_size(B, H, Nq).  Returns 0 for arguments attn_bwd would
@@ -179,7 +184,7 @@ enum attn_pass {
 /*
  * attn_bwd_fused -- 1 when attn_bwd runs as ONE fused kernel for these
  * arguments, else 0 (also 0 for arguments attn_bwd would reject).  Fused:
- * bf16 block-local attention whose window divides 64 and whose query rows per
+ * bf16 or fp16 block-local attention whose window divides 64 and whose query rows per
  * window Wq = Nq / (Nk / window) divide the window (Wq = window, or pooled
  * queries with an integer q_stride = window / Wq), where every query row
  * sees keys of its own 64-key tile only ("hiera-optim 0.1.0" sdist,

@@ -13,7 +13,7 @@ from oracle.attention import visible
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, ALIAS, DEVICE, LAUNCH = range(8)
-BF16, FP32 = 0, 1
+BF16, FP32, FP16 = 0, 1, 2
 MASK = {"none": 0, "causal": 1, "sliding": 2, "block": 3}
 
 
@@ -100,6 +100,7 @@ def test_pooled_block_single_tile_dispatch(lib):
     assert lib.attn_bwd_fused(0, 1, 1, 12, 64, 96, 3, 16) == 0        # 3 rows per window of 16
     assert lib.attn_bwd_fused(0, 1, 1, 20, 80, 96, 3, 80) == 0        # window 80 does not divide 64
     assert lib.attn_bwd_fused(1, 1, 1, 784, 3136, 96, 3, 64) == 0     # fp32
+    assert lib.attn_bwd_fused(2, 1, 1, 784, 3136, 96, 3, 64) == 1     # fp16
     assert lib.attn_bwd_fused(0, 1, 1, 15, 64, 96, 3, 16) == 0        # invalid: 4 windows, 15 rows
 
 
@@ -107,6 +108,7 @@ def test_workspace_size_ds_where_it_does_not_apply(lib):
     base = lib.attn_bwd_workspace_size(1, 2, 256)
     assert lib.attn_bwd_workspace_size_ds(0, 1, 2, 256, 256, 96, 1, 0) == base     # d != 128
     assert lib.attn_bwd_workspace_size_ds(1, 1, 2, 256, 256, 128, 1, 0) == base    # fp32
+    assert lib.attn_bwd_workspace_size_ds(2, 1, 2, 256, 256, 128, 1, 0) > base     # fp16 keeps dS
     assert lib.attn_bwd_workspace_size_ds(0, 1, 2, 256, 256, 128, 3, 64) == base   # fused block-local
     assert lib.attn_bwd_workspace_size_ds(0, 1, 2, 256, 256, 128, 3, 5) == 0       # invalid window
     # the causal N=8192, H=20 workload: 256 * 257 / 2 blocks per head
@@ -154,12 +156,15 @@ def test_valid_arguments_pass(lib):
         assert check_fwd(lib, mask=mask, window=window) == OK
         assert check_bwd(lib, mask=mask, window=window) == OK
     assert check_fwd(lib, dtype=FP32, d=96) == OK
+    assert check_fwd(lib, dtype=FP16, d=128) == OK
+    assert check_bwd(lib, dtype=FP16, mask=1) == OK
     assert check_fwd(lib, Nq=7, Nk=300, mask=1) == OK          # Nq != Nk, top-left causal
     assert check_fwd(lib, Nq=50, Nk=100, mask=3, window=4) == OK  # pooled: 25 windows of 2 rows x 4 keys
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=2), UNSUPPORTED),
+    (dict(dtype=3), UNSUPPORTED),
+    (dict(dtype=-1), UNSUPPORTED),
     (dict(d=80), UNSUPPORTED),
     (dict(d=256), UNSUPPORTED),
     (dict(B=0), INVALID),
