@@ -12,6 +12,9 @@ no tiling and no online rescaling:
   * ``attention.visible``     -- the visibility predicate of the four mask modes
   * ``attention.oracle_fwd``  -- O and the per-row natural-log logsumexp
   * ``attention.oracle_bwd``  -- dQ, dK, dV of L = <O, dO>
+  * ``premix.premix_fwd``     -- IHA pseudo-token construction
+                                 Out[h, p] = sum_s W[h, p, s] X[s]
+  * ``premix.premix_bwd``     -- its dX = W^T dOut and dW = sum dOut X^T
   * ``brute``                 -- scalar loops with math.fsum for tiny inputs,
                                  used only to pin the vectorised functions
 
@@ -20,5 +23,7 @@ force, torch's own fp64 ``scaled_dot_product_attention`` with autograd,
 central finite differences, closed forms and invariants.
 """
 from .attention import MASKS, visible, oracle_fwd, oracle_bwd
+from .premix import premix_bwd, premix_fwd, pseudo_tokens
 
-__all__ = ["MASKS", "visible", "oracle_fwd", "oracle_bwd"]
+__all__ = ["MASKS", "visible", "oracle_fwd", "oracle_bwd", "premix_fwd", "premix_bwd",
+           "pseudo_tokens"]

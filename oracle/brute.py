@@ -58,3 +58,26 @@ def brute_fwd(q, k, v, scale, mask="none", window=0, window_q=0):
         o.append(ob)
         lse.append(lb)
     return o, lse
+
+
+def brute_premix(x, w):
+    """IHA premix by scalar loops: x nested [B][N][H][d], w [H][P][H].
+    Returns out [B][H][N][P][d] with out[b][h][n][p][c] = fsum over s of
+    w[h][p][s] * x[b][n][s][c]."""
+    B, N, H, d = len(x), len(x[0]), len(x[0][0]), len(x[0][0][0])
+    P = len(w[0])
+    return [[[[[math.fsum(w[h][p][s] * x[b][n][s][c] for s in range(H)) for c in range(d)]
+               for p in range(P)] for n in range(N)] for h in range(H)] for b in range(B)]
+
+
+def brute_premix_bwd(x, w, dout):
+    """dX[b][n][s][c] = fsum over (h, p) of w[h][p][s] * dout[b][h][n][p][c];
+    dW[h][p][s] = fsum over (b, n, c) of dout[b][h][n][p][c] * x[b][n][s][c]."""
+    B, N, H, d = len(x), len(x[0]), len(x[0][0]), len(x[0][0][0])
+    P = len(w[0])
+    dx = [[[[math.fsum(w[h][p][s] * dout[b][h][n][p][c] for h in range(H) for p in range(P))
+             for c in range(d)] for s in range(H)] for n in range(N)] for b in range(B)]
+    dw = [[[math.fsum(dout[b][h][n][p][c] * x[b][n][s][c]
+                      for b in range(B) for n in range(N) for c in range(d))
+            for s in range(H)] for p in range(P)] for h in range(H)]
+    return dx, dw
