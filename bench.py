@@ -110,6 +110,26 @@ def kernel_work(w, pairs_per_bh: int, kept_ds: bool = False) -> dict:
         # dK, dV (its row sums come from P and dP in-tile, O is not read)
         "bwd": dict(flops=10 * d * pairs,
                     bytes=(3 * q_rows * d + 4 * k_rows * d) * es + 4 * q_rows),
+    } | premix_work(w, es)
+
+
+def premix_work(w, es: int) -> dict:
+    """IHA premix of Q, K and V (three launches each way): per tensor the
+    forward reads X [B][N][H][d] and W and writes the B*H*N*P*d pseudo-token
+    elements (2 H flops each); the backward reads X and dOut, writes dX (2 H P
+    flops per element) and dW (2 per pseudo-token element), plus the fp32 dW
+    partials written and read once."""
+    if w.P <= 1:
+        return {}
+    N = w.Nq // w.P
+    x = w.B * N * w.H * w.d
+    y = x * w.P
+    wt = w.H * w.P * w.H
+    part = min(w.B * N, 1024) * wt * 4
+    return {
+        "premix": dict(flops=3 * 2 * w.H * y, bytes=3 * ((x + y + wt) * es)),
+        "premix_bwd": dict(flops=3 * (2 * w.H * w.P * x + 2 * y * w.H),
+                           bytes=3 * ((2 * x + y + wt) * es + 2 * part + wt * 4)),
     }
 
 
@@ -141,6 +161,39 @@ def stored_traffic(workload: str, kernel: str):
         return None
     val = fields.get(f"traffic_bytes_per_launch.{kernel}")
     return float(val) if val is not None else None
+
+
+# ------------------------------------------------------- interleaved heads
+
+def iha_setup(attn, torch, w, dev):
+    """Inputs of the IHA premix for Q, K, V (seeds 100, 101, 102), their
+    pseudo-token outputs and the backward's buffers."""
+    from head_attention_attn_amd.inputs import make_premix_inputs
+    N = w.Nq // w.P
+    xs, ws = [], []
+    for i in range(3):
+        x, wt, _ = make_premix_inputs(w.B, N, w.H, w.P, w.d, w.dtype, seed=100 + i)
+        xs.append(x.to(dev))
+        ws.append(wt.to(dev))
+    out = [attn.binding.premix(x, wt) for x, wt in zip(xs, ws)]
+    torch.cuda.synchronize(dev)
+    return {"x": xs, "w": ws, "out": out,
+            "dx": [torch.empty_like(x) for x in xs],
+            "dw": [torch.empty((w.H, w.P, w.H), dtype=torch.float32, device=dev) for _ in xs],
+            "ws": torch.empty(attn.binding.premix_workspace_bytes(w.B, N, w.H, w.P),
+                              dtype=torch.uint8, device=dev)}
+
+
+def premix_parity(iha, w, npos: int = 32):
+    """The first ``npos`` positions of the Q premix against the oracle:
+    max |gpu - ref| / (2^-8 |ref| + 1e-6), the bf16 output-rounding bound."""
+    import numpy as np
+    from oracle.premix import premix_fwd
+    x = iha["x"][0][:, :npos].double().cpu().numpy()
+    wt = iha["w"][0].double().cpu().numpy()
+    ref = premix_fwd(x, wt)
+    got = iha["out"][0][:, :, :npos].double().cpu().numpy()
+    return float(np.max(np.abs(got - ref) / (2.0 ** -8 * np.abs(ref) + 1e-6)))
 
 
 # ------------------------------------------------------- Hiera token order
@@ -331,6 +384,13 @@ def main() -> int:
 
     host = workload_inputs(w, seed=0)
     q, k, v, do = (t.to(dev) for t in host)
+    iha = None
+    if w.P > 1:
+        # interleaved head attention: the attention's Q, K, V are the premix
+        # outputs (each head's N * P pseudo-tokens) of three [B, N, H, d]
+        # inputs; the drawn q, k, v serve only as the first step's values
+        iha = iha_setup(attn, torch, w, dev)
+        q, k, v = (t.view(w.B, w.H, w.Nq, w.d) for t in iha["out"])
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -343,9 +403,18 @@ def main() -> int:
 
     fused = attn.binding.bwd_fused(q, k, v, mask=w.mask, window=w.window)
     kernels = ("fwd", "bwd") if fused else KERNELS
+    if iha is not None:
+        kernels = ("premix",) + kernels + ("premix_bwd",)
 
     def launch(kernel):
-        if kernel == "fwd":
+        if kernel == "premix":
+            for x, wt, out in zip(iha["x"], iha["w"], iha["out"]):
+                attn.binding.premix(x, wt, out=out)
+        elif kernel == "premix_bwd":
+            for x, wt, g, dx, dw in zip(iha["x"], iha["w"], (dq, dk, dv), iha["dx"], iha["dw"]):
+                attn.binding.premix_bwd(x, wt, g.view(iha["out"][0].shape), dx=dx, dw=dw,
+                                        workspace=iha["ws"])
+        elif kernel == "fwd":
             attn.fwd(q, k, v, out=o, lse=lse, **kw)
         elif kernel == "bwd":
             attn.bwd(q, k, v, o, lse, do, workspace=ws, dq=dq, dk=dk, dv=dv, **kw)
@@ -389,6 +458,14 @@ def main() -> int:
         def ag_step():
             oa = attn.fused_attention(qa, ka, va, w.mask, w.window, w.scale)
             return torch.autograd.grad(oa, (qa, ka, va), do)
+
+        if iha is not None:
+            # the whole interleaved-head step: premix, attention, both backwards
+            leaves = [t.detach().requires_grad_(True) for t in iha["x"] + iha["w"]]
+
+            def ag_step():
+                oa = attn.iha_attention(*leaves, window=w.window, scale=w.scale)
+                return torch.autograd.grad(oa, leaves, do)
 
         for _ in range(3):
             ag_step()
@@ -461,6 +538,10 @@ def main() -> int:
 
     cpu = None
     parity = {"staged_equals_attn_bwd": bool(same)}
+    if iha is not None:
+        # the attention's inputs are the premix outputs
+        host = tuple(t.cpu() for t in (q, k, v)) + (host[3],)
+        parity["premix_error_over_bound"] = round(premix_parity(iha, w), 4)
     if args.cpu_seconds > 0:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
         cpu, par = cpu_baseline(w, host, pairs_bh, args.cpu_seconds, gpu_out)
@@ -474,6 +555,10 @@ def main() -> int:
                     if fused else
                     "attn_fwd + attn_bwd (row sums, dK/dV keeping dS, dQ = scale dS K)"
                     if kept_ds else "attn_fwd + attn_bwd (row sums, dK/dV, dQ passes)")}
+    if iha is not None:
+        cfg.update(P=w.P, tokens=w.Nq // w.P,
+                   step="attn_premix_fwd x3 (Q, K, V pseudo-tokens) + " + cfg["step"]
+                        + " over the N * P pseudo-tokens + attn_premix_bwd x3 (dX, dW)")
     rec = {
         "metric": "attention fwd+bwd TFLOP/s at 1 MI355X; % of bf16 MFMA peak",
         "value": round(value, 3),
@@ -501,6 +586,7 @@ def main() -> int:
     }
     print(json.dumps(rec), flush=True)
     ok = same and parity.get("pass", True) and (layout_rec is None or layout_rec["bitwise_equal"])
+    ok = ok and parity.get("premix_error_over_bound", 0.0) <= 1.0
     return 0 if ok else 1
 
 

@@ -76,3 +76,37 @@ class FusedAttention(torch.nn.Module):
 
     def extra_repr(self) -> str:
         return f"mask={self.mask!r}, window={self.window}, scale={self.scale}"
+
+
+class PremixFunction(torch.autograd.Function):
+    """IHA pseudo-token construction out = premix(x, w) ("IHA-CUDA",
+    Pseudo-Token Mixing) with its backward from ``attn_premix_bwd``: x
+    [B, N, H, d], w [H, P, H] (x's dtype) -> [B, H, N, P, d]."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        ctx.save_for_backward(x, w)
+        return binding.premix(x, w)
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, w = ctx.saved_tensors
+        dx, dw = binding.premix_bwd(x, w, dout.to(x.dtype).contiguous())
+        return dx, dw.to(w.dtype)
+
+
+def premix(x, w):
+    """Differentiable IHA premix (see ``PremixFunction``)."""
+    return PremixFunction.apply(x, w)
+
+
+def iha_attention(xq, xk, xv, wq, wk, wv, window: int, scale=None):
+    """Interleaved head attention: Q, K, V premixed into P pseudo-heads per
+    head, then one causal sliding-window attention of ``window`` pseudo-tokens
+    over each head's N * P pseudo-tokens (the joint softmax across
+    pseudo-heads).  x* [B, N, H, d], w* [H, P, H]; returns O [B, H, N * P, d]
+    (pseudo-token t = n * P + p)."""
+    B, N, H, d = xq.shape
+    P = wq.shape[1]
+    q, k, v = (premix(x, w).view(B, H, N * P, d) for x, w in ((xq, wq), (xk, wk), (xv, wv)))
+    return fused_attention(q, k, v, "sliding", window, scale)

@@ -87,6 +87,18 @@ def load_library():
     lib.attn_check_bwd_strided.restype = ctypes.c_int
     lib.attn_layouts_contiguous.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64, lp]
     lib.attn_layouts_contiguous.restype = ctypes.c_int
+    lib.attn_premix_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp, vp]
+    lib.attn_premix_fwd.restype = ctypes.c_int
+    lib.attn_premix_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp, vp, fp, vp,
+                                    ctypes.c_size_t, vp]
+    lib.attn_premix_bwd.restype = ctypes.c_int
+    lib.attn_premix_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+    lib.attn_premix_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_check_premix_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp]
+    lib.attn_check_premix_fwd.restype = ctypes.c_int
+    lib.attn_check_premix_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp, vp, fp,
+                                          vp, ctypes.c_size_t]
+    lib.attn_check_premix_bwd.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -275,3 +287,59 @@ def bwd(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
     if st != 0:
         raise AttnError(st, "attn_bwd_passes")
     return dq, dk, dv
+
+
+# ------------------------------------------------------------ IHA premix
+
+def _premix_shapes(x, w):
+    if x.dim() != 4 or w.dim() != 3:
+        raise ValueError("x must be [B, N, H, d] and w [H, P, H]")
+    B, N, H, d = x.shape
+    if w.shape[0] != H or w.shape[2] != H:
+        raise ValueError(f"w{tuple(w.shape)} does not match H = {H}")
+    if x.dtype not in DTYPE_CODES or w.dtype != x.dtype:
+        raise ValueError("x and w must share a 16-bit dtype")
+    for t in (x, w):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("premix tensors must be contiguous device tensors")
+    return B, N, H, w.shape[1], d
+
+
+def premix_workspace_bytes(B: int, N: int, H: int, P: int) -> int:
+    return int(load_library().attn_premix_bwd_workspace_size(B, N, H, P))
+
+
+def premix(x, w, out=None):
+    """IHA pseudo-tokens: out[b, h, n, p] = sum_s w[h, p, s] x[b, n, s]
+    (``attn_premix_fwd``).  x [B, N, H, d], w [H, P, H] -> out
+    [B, H, N, P, d]; ``out.view(B, H, N * P, d)`` is each head's pseudo-token
+    sequence."""
+    lib = load_library()
+    B, N, H, P, d = _premix_shapes(x, w)
+    if out is None:
+        out = torch.empty((B, H, N, P, d), dtype=x.dtype, device=x.device)
+    st = lib.attn_premix_fwd(DTYPE_CODES[x.dtype], B, N, H, P, d, x.data_ptr(), w.data_ptr(),
+                             out.data_ptr(), _stream(x))
+    if st != 0:
+        raise AttnError(st, "attn_premix_fwd")
+    return out
+
+
+def premix_bwd(x, w, dout, dx=None, dw=None, workspace=None):
+    """dx = w^T dout, dw = sum over (b, n, feature) of dout x^T
+    (``attn_premix_bwd``); dw is float32."""
+    lib = load_library()
+    B, N, H, P, d = _premix_shapes(x, w)
+    if tuple(dout.shape) != (B, H, N, P, d) or dout.dtype != x.dtype or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous [B, H, N, P, d] tensor of x's dtype")
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty((H, P, H), dtype=torch.float32, device=x.device) if dw is None else dw
+    if workspace is None:
+        workspace = torch.empty(premix_workspace_bytes(B, N, H, P), dtype=torch.uint8,
+                                device=x.device)
+    st = lib.attn_premix_bwd(DTYPE_CODES[x.dtype], B, N, H, P, d, x.data_ptr(), w.data_ptr(),
+                             dout.data_ptr(), dx.data_ptr(), dw.data_ptr(), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream(x))
+    if st != 0:
+        raise AttnError(st, "attn_premix_bwd")
+    return dx, dw

@@ -361,6 +361,37 @@ attn::RowMap rowmap(const attn_layout& lay, int64_t n, int64_t T) {
   return rm;
 }
 
+// ------------------------------------------------------------ IHA premix
+
+constexpr int64_t kPremixMaxH = 32;    // source heads (one MFMA column)
+constexpr int64_t kPremixMaxHP = 128;  // pseudo-heads H * P (four MFMA tiles)
+constexpr int64_t kPremixGrid = 1024;  // workgroups, and dW partials, per call
+
+int premix_grid(int64_t B, int64_t N) { return (int)std::min<int64_t>(B * N, kPremixGrid); }
+
+int check_premix_geometry(int dtype, int64_t B, int64_t N, int64_t H, int64_t P, int64_t d) {
+  if (!is16(dtype)) return ATTN_ERR_UNSUPPORTED;
+  if (B < 1 || N < 1 || H < 1 || P < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  if (H > kPremixMaxH || H * P > kPremixMaxHP || (P & (P - 1))) return ATTN_ERR_UNSUPPORTED;
+  if (N > kMaxSeq || B * N > (int64_t(1) << 40)) return ATTN_ERR_INVALID_ARG;
+  // row offsets of one batch's output in 31 bits
+  if (H * N * P * d >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+attn::PremixArgs premix_args(int64_t B, int64_t N, int64_t H, int64_t P) {
+  attn::PremixArgs a{};
+  a.B = (int)B;
+  a.N = (int)N;
+  a.H = (int)H;
+  int lp = 0;
+  while ((int64_t(1) << lp) < P) ++lp;
+  a.lp = lp;
+  a.grid = premix_grid(B, N);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -535,6 +566,76 @@ int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
              void* workspace, size_t workspace_bytes, void* stream) {
   return attn_bwd_passes(ATTN_PASS_ALL, dtype, B, H, Nq, Nk, d, scale, mask, window, q, k, v, o,
                          lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------ IHA premix
+
+size_t attn_premix_bwd_workspace_size(int64_t B, int64_t N, int64_t H, int64_t P) {
+  if (B < 1 || N < 1 || H < 1 || P < 1 || H > kPremixMaxH || H * P > kPremixMaxHP) return 0;
+  const size_t raw = (size_t)premix_grid(B, N) * (size_t)(H * P * H) * sizeof(float);
+  return (raw + 255) & ~size_t(255);
+}
+
+int attn_check_premix_fwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P, int64_t d,
+                          const void* x, const void* w, const void* out) {
+  int st = check_premix_geometry(dtype, B, N, H, P, d);
+  if (st) return st;
+  const size_t es = elem_size(dtype);
+  const Arg ins[2] = {flat_arg(x, (size_t)(B * N * H * d) * es), flat_arg(w, (size_t)(H * P * H) * es)};
+  const Arg outs[1] = {flat_arg(out, (size_t)(B * H * N * P * d) * es)};
+  return check_args(ins, 2, outs, 1, Shape{B, H, d, es});
+}
+
+int attn_check_premix_bwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P, int64_t d,
+                          const void* x, const void* w, const void* dout, const void* dx,
+                          const float* dw, const void* workspace, size_t workspace_bytes) {
+  int st = check_premix_geometry(dtype, B, N, H, P, d);
+  if (st) return st;
+  const size_t es = elem_size(dtype);
+  const Arg ins[3] = {flat_arg(x, (size_t)(B * N * H * d) * es),
+                      flat_arg(w, (size_t)(H * P * H) * es),
+                      flat_arg(dout, (size_t)(B * H * N * P * d) * es)};
+  if (!workspace || workspace_bytes < attn_premix_bwd_workspace_size(B, N, H, P))
+    return ATTN_ERR_WORKSPACE;
+  const Arg outs[3] = {flat_arg(dx, (size_t)(B * N * H * d) * es),
+                       flat_arg(dw, (size_t)(H * P * H) * sizeof(float)),
+                       flat_arg(workspace, attn_premix_bwd_workspace_size(B, N, H, P))};
+  return check_args(ins, 3, outs, 3, Shape{B, H, d, es});
+}
+
+int attn_premix_fwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P, int64_t d,
+                    const void* x, const void* w, void* out, void* stream) {
+  int st = attn_check_premix_fwd(dtype, B, N, H, P, d, x, w, out);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  attn::PremixArgs a = premix_args(B, N, H, P);
+  a.x = x;
+  a.w = w;
+  a.out = out;
+  const int err = attn::launch_premix_fwd(a, dtype == ATTN_FP16, (int)d,
+                                          static_cast<hipStream_t>(stream));
+  return err ? ATTN_ERR_LAUNCH : ATTN_OK;
+}
+
+int attn_premix_bwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P, int64_t d,
+                    const void* x, const void* w, const void* dout, void* dx, float* dw,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = attn_check_premix_bwd(dtype, B, N, H, P, d, x, w, dout, dx, dw, workspace,
+                                 workspace_bytes);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  attn::PremixArgs a = premix_args(B, N, H, P);
+  a.x = x;
+  a.w = w;
+  a.dout = dout;
+  a.dx = dx;
+  a.dw = dw;
+  a.dw_part = static_cast<float*>(workspace);
+  const int err = attn::launch_premix_bwd(a, dtype == ATTN_FP16, (int)d,
+                                          static_cast<hipStream_t>(stream));
+  return err ? ATTN_ERR_LAUNCH : ATTN_OK;
 }
 
 const char* attn_status_string(int status) {

@@ -63,7 +63,7 @@ __device__ __forceinline__ LocalTile local_tile(int tile, int nq, int lw, int lq
 
 // QR: query buffer rows (32 when QT <= 32, else 64); one wave per 32 rows
 template <typename E, int D, int QR, bool SR>
-__global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
+__global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(QR == 32 ? 1 : D == 128 ? 2 : 3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
   using V8 = typename E::v8;
   constexpr int NT = 2 * QR, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[TE];

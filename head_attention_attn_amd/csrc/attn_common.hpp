@@ -208,6 +208,21 @@ struct BwdArgs {
   MaskGeom mg;
 };
 
+// IHA premix (pseudo-token construction) and its backward.  x, dx
+// [B][N][H][d]; w [H][P][H] (input type); out, dout [B][H][N][P][d]; dw
+// [H][P][H] fp32; dw_part: `grid` partial dW blocks of H*P*H fp32.
+struct PremixArgs {
+  const void* x;
+  const void* w;
+  void* out;
+  const void* dout;
+  void* dx;
+  float* dw;
+  float* dw_part;
+  int B, N, H, lp;  // lp = log2(P)
+  int grid;         // workgroups; also the number of dW partials
+};
+
 // every tensor of a call in the contiguous layout (the SR = false kernels)
 inline bool rows_plain(const FwdArgs& a, int d) {
   return a.rq.plain(a.H, a.nq, d) && a.rk.plain(a.H, a.nk, d) && a.rv.plain(a.H, a.nk, d) &&
@@ -237,5 +252,8 @@ int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s);
 int launch_fwd_16_local(const FwdArgs& a, bool f16, int d, hipStream_t s);
 int launch_bwd_16_local(const BwdArgs& a, bool f16, int d, hipStream_t s);
 int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s, int passes);
+// IHA premix (16-bit types)
+int launch_premix_fwd(const PremixArgs& a, bool f16, int d, hipStream_t s);
+int launch_premix_bwd(const PremixArgs& a, bool f16, int d, hipStream_t s);
 }  // namespace attn
 #endif

@@ -38,6 +38,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // element types of the 16-bit kernels
 struct Bf16 {
+  typedef __bf16 scalar;
   typedef bf16x8 v8;
   typedef bf16x4 v4;
   static __device__ __forceinline__ f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
@@ -46,6 +47,7 @@ struct Bf16 {
 };
 
 struct F16 {
+  typedef _Float16 scalar;
   typedef f16x8 v8;
   typedef f16x4 v4;
   static __device__ __forceinline__ f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {

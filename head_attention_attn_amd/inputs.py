@@ -30,6 +30,12 @@ are synthetic i.i.d. N(0, 1)):
   ("IHA-CUDA", End-to-End Training Benchmark).
 * sliding_pseudo_head -- causal sliding window W = 1024 (WSL = 1023) over
   20 heads x 4 pseudo-heads at N=4096 ("IHA-CUDA", FLOP Matching).
+* iha_joint -- interleaved head attention with the joint softmax: the
+  20-head d=128 LLaMA at N = 8192 tokens, P = 4 pseudo-heads built by the
+  premix from Q, K, V (W ~ N(0, 1/H)), and one causal sliding window of
+  W = WSL + 1 = 1024 pseudo-tokens over each head's 32768 pseudo-tokens
+  ("IHA-CUDA", End-to-End Training Benchmark and FLOP Matching, N = 8192
+  row).
 """
 from __future__ import annotations
 
@@ -50,6 +56,7 @@ class Workload:
     dtype: str          # "bf16", "fp16" or "fp32"
     mask: str           # "none" | "causal" | "sliding" | "block"
     window: int = 0
+    P: int = 1          # IHA pseudo-heads: Nq = Nk = N * P pseudo-tokens built by the premix
 
     @property
     def scale(self) -> float:
@@ -69,6 +76,7 @@ WORKLOADS = {
         Workload("global_vision", 128, 4, 196, 196, 96, "bf16", "none"),
         Workload("causal_lm", 1, 20, 8192, 8192, 128, "bf16", "causal"),
         Workload("sliding_pseudo_head", 1, 80, 4096, 4096, 128, "bf16", "sliding", 1024),
+        Workload("iha_joint", 1, 20, 32768, 32768, 128, "bf16", "sliding", 1024, 4),
     )
 }
 
@@ -91,3 +99,17 @@ def make_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str = "bf16",
 
 def workload_inputs(w: Workload, seed: int = 0):
     return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, seed)
+
+
+def make_premix_inputs(B: int, N: int, H: int, P: int, d: int, dtype: str = "bf16",
+                       seed: int = 0):
+    """CPU tensors (x, w, dout) of an IHA premix: x [B, N, H, d] ~ N(0, 1),
+    w [H, P, H] ~ N(0, 1/H) (so that each pseudo-head output has unit
+    variance), dout [B, H, N, P, d] ~ N(0, 1); one generator seeded with
+    ``seed``, drawn in that order in fp32, then rounded to ``dtype``."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn((B, N, H, d), dtype=torch.float32, generator=g)
+    w = torch.randn((H, P, H), dtype=torch.float32, generator=g) / math.sqrt(H)
+    dout = torch.randn((B, H, N, P, d), dtype=torch.float32, generator=g)
+    tdt = TORCH_DTYPES[dtype]
+    return x.to(tdt), w.to(tdt), dout.to(tdt)

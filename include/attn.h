@@ -330,6 +330,58 @@ ATTN_API int attn_check_bwd_strided(int dtype, int64_t B, int64_t H, int64_t Nq,
                                     const void* workspace, size_t workspace_bytes,
                                     const attn_layouts* layouts);
 
+/*
+ * IHA premix -- pseudo-token construction of Interleaved Head Attention
+ * ("IHA-CUDA: Interleaved Head Attention Kernels for Hopper GPUs", section
+ * "Pseudo-Token Mixing"): Q, K and V are each mixed across heads before
+ * attention,
+ *     Out[h, p] = sum_s W[h, p, s] * X[s]
+ * a linear map from H source heads to H x P pseudo-heads at every (batch,
+ * position, feature).  Layouts (contiguous):
+ *     x, dx     [B][N][H][d]      e.g. a projection output
+ *     w         [H][P][H]         W[h][p][s], element type `dtype`
+ *     out, dout [B][H][N][P][d]   per head the N * P pseudo-tokens in the
+ *                                 order t = n * P + p
+ *     dw        [H][P][H]         fp32
+ * Attention over each head's pseudo-token sequence (attn_fwd with Nq = Nk =
+ * N * P on `out` read as [B][H][N * P][d]) is IHA's joint softmax across the
+ * P pseudo-heads; the pages' FLOP matching uses a causal sliding window of
+ * W = WSL + 1 = N / (2P) pseudo-tokens.
+ * dtype: ATTN_BF16 or ATTN_FP16 (ATTN_ERR_UNSUPPORTED otherwise), fp32
+ * accumulation, outputs rounded to nearest even.  d in {64, 96, 128};
+ * H <= 32, H * P <= 128, P a power of two (ATTN_ERR_UNSUPPORTED otherwise);
+ * H * N * P * d < 2^31 (ATTN_ERR_INVALID_ARG).  Pointers 16-byte aligned;
+ * outputs may not overlap inputs or each other.
+ */
+ATTN_API int attn_premix_fwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P, int64_t d,
+                             const void* x, const void* w, void* out, void* stream);
+
+/*
+ * attn_premix_bwd_workspace_size -- bytes of fp32 workspace attn_premix_bwd
+ * needs: one H*P*H partial dW per workgroup (min(B*N, 1024) of them),
+ * rounded up to 256.  0 for unsupported H, P or sizes < 1.
+ */
+ATTN_API size_t attn_premix_bwd_workspace_size(int64_t B, int64_t N, int64_t H, int64_t P);
+
+/*
+ * attn_premix_bwd -- dx = W^T dout (the transposed map) and dw = sum over
+ * (b, n, feature) of dout * x^T, for the same arguments as attn_premix_fwd.
+ * dw is reduced without atomics: each workgroup writes a partial sum to the
+ * workspace (contents on entry ignored) and a second kernel adds them in a
+ * fixed order, so results are bitwise deterministic.
+ */
+ATTN_API int attn_premix_bwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P, int64_t d,
+                             const void* x, const void* w, const void* dout, void* dx,
+                             float* dw, void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_check_premix_fwd / attn_check_premix_bwd -- their validation alone. */
+ATTN_API int attn_check_premix_fwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P,
+                                   int64_t d, const void* x, const void* w, const void* out);
+ATTN_API int attn_check_premix_bwd(int dtype, int64_t B, int64_t N, int64_t H, int64_t P,
+                                   int64_t d, const void* x, const void* w, const void* dout,
+                                   const void* dx, const float* dw, const void* workspace,
+                                   size_t workspace_bytes);
+
 /* attn_status_string -- static, human-readable name of a status code. */
 ATTN_API const char* attn_status_string(int status);
 

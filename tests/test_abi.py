@@ -36,7 +36,9 @@ def test_header_declares_the_entry_points():
                                          "attn_check_fwd", "attn_check_bwd", "attn_status_string",
                                          "attn_layouts_contiguous", "attn_fwd_strided",
                                          "attn_bwd_strided", "attn_check_fwd_strided",
-                                         "attn_check_bwd_strided"])
+                                         "attn_check_bwd_strided", "attn_premix_fwd",
+                                         "attn_premix_bwd", "attn_premix_bwd_workspace_size",
+                                         "attn_check_premix_fwd", "attn_check_premix_bwd"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -219,3 +221,30 @@ def test_fused_backward_predicate(lib):
     assert f(BF16, 3136, 2, 64) == 0            # sliding
     assert f(BF16, 100, 3, 64) == 0             # 100 % 64 != 0: invalid geometry
     assert f(BF16, 128, 3, 64, d=80) == 0       # unsupported d
+
+
+def test_premix_validation(lib):
+    B, N, H, P, d = 1, 64, 20, 4, 128
+    x, w, out, dout, dx, dw, ws = ptrs(7)
+    ck = lambda dtype=BF16, **kw: lib.attn_check_premix_fwd(
+        dtype, kw.get("B", B), kw.get("N", N), kw.get("H", H), kw.get("P", P), kw.get("d", d),
+        kw.get("x", x), kw.get("w", w), kw.get("out", out))
+    assert ck() == OK
+    assert ck(FP16) == OK
+    assert ck(FP32) == UNSUPPORTED                       # 16-bit MFMA path only
+    assert ck(H=33) == UNSUPPORTED and ck(H=20, P=8) == UNSUPPORTED and ck(P=3) == UNSUPPORTED
+    assert ck(d=80) == UNSUPPORTED
+    assert ck(N=0) == INVALID and ck(x=0) == INVALID
+    assert ck(N=1 << 20, H=32, P=4) == INVALID           # H*N*P*d >= 2^31
+    assert ck(w=BASE + 8) == MISALIGNED
+    assert ck(out=x + 128) == ALIAS                      # output inside x
+    wsz = lib.attn_premix_bwd_workspace_size(B, N, H, P)
+    assert wsz == ((min(B * N, 1024) * H * P * H * 4 + 255) // 256) * 256
+    assert lib.attn_premix_bwd_workspace_size(4, 8192, H, P) == 1024 * H * P * H * 4
+    assert lib.attn_premix_bwd_workspace_size(1, 1, 33, 1) == 0
+    cb = lambda **kw: lib.attn_check_premix_bwd(BF16, B, N, H, P, d, x, w, kw.get("dout", dout),
+                                                kw.get("dx", dx), kw.get("dw", dw), kw.get("ws", ws),
+                                                kw.get("wsz", wsz))
+    assert cb() == OK
+    assert cb(wsz=wsz - 1) == WORKSPACE and cb(ws=0) == WORKSPACE
+    assert cb(dx=dout) == ALIAS and cb(dw=dx + 16) == ALIAS

@@ -74,3 +74,21 @@ def test_kept_ds_bytes():
     assert kept["dkdv"]["bytes"] == plain["dkdv"]["bytes"] + 2 * pairs
     assert kept["dq"]["bytes"] == rows * w.d * 2 * 2 + 2 * pairs
     assert kept["dq"]["flops"] == plain["dq"]["flops"]
+
+
+def test_iha_workload_accounting():
+    """The IHA workload: 20 heads, 8192 tokens x 4 pseudo-heads = 32768
+    pseudo-tokens, a causal window of 1024 pseudo-tokens (the pages' N = 8192
+    row: WSL = N / (2P) - 1 = 1023); the premix moves, per Q/K/V tensor, the
+    [B, N, H, d] input and the P times larger pseudo-token output."""
+    w = WORKLOADS["iha_joint"]
+    N = w.Nq // w.P
+    assert (w.H, N, w.P, w.window, w.Nq) == (20, 8192, 4, 1024, 32768)
+    assert w.window == N // (2 * w.P)
+    pairs = bench.visible_pairs(w.mask, w.window, w.Nq, w.Nk)
+    assert pairs == 32768 * 1024 - 1024 * 1023 // 2
+    work = bench.kernel_work(w, pairs)
+    x = N * 20 * 128
+    assert work["premix"]["bytes"] == 3 * 2 * (x + 4 * x + 20 * 4 * 20)
+    assert work["premix"]["flops"] == 3 * 2 * 20 * (4 * x)
+    assert "premix" not in bench.kernel_work(WORKLOADS["causal_lm"], 1)
