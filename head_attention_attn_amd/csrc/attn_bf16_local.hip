@@ -30,6 +30,10 @@
 #include "attn_common.hpp"
 #include "bf16_tile.hpp"
 
+// The forward's waves-per-EU attribute is a register budget; LDS limits some
+// instances (wide d, 32-row query tiles) below it, which the compiler reports.
+#pragma clang diagnostic ignored "-Wpass-failed"
+
 namespace attn {
 
 namespace {
@@ -46,7 +50,8 @@ struct LocalTile {
   int lw, lq, qt;  // log2 w, log2 wq, query rows per tile
   int tq0, qend;   // first query row of the tile, end of its real rows
   __device__ __forceinline__ bool real(int r) const { return tq0 + r < qend; }  // implies r < qt
-  __device__ __forceinline__ bool vis(int r, int c) const { return real(r) && (r >> lq) == (c >> lw); }
+  // bitwise, not short-circuit: evaluated per score element without branches
+  __device__ __forceinline__ bool vis(int r, int c) const { return real(r) & ((r >> lq) == (c >> lw)); }
 };
 
 __device__ __forceinline__ LocalTile local_tile(int tile, int nq, int lw, int lq) {
@@ -63,7 +68,7 @@ __device__ __forceinline__ LocalTile local_tile(int tile, int nq, int lw, int lq
 
 // QR: query buffer rows (32 when QT <= 32, else 64); one wave per 32 rows
 template <typename E, int D, int QR, bool SR>
-__global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(QR == 32 ? 1 : D == 128 ? 2 : 3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
+__global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
   using V8 = typename E::v8;
   constexpr int NT = 2 * QR, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
@@ -210,17 +215,23 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
                        y[mb]);
       }
     }
-    float dsum = 0.f;
+    float dsum = with_mask(!full, [&](auto masked) {
+      float sum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
-        const bool vis = full || lt.vis(own, key);
-        const float p = vis ? fast_exp2(fmaf(x[mb][e], sl2, -lse2)) : 0.f;
-        x[mb][e] = p;
-        dsum = fmaf(p, y[mb][e], dsum);
-      }
+        for (int e = 0; e < 16; ++e) {
+          float arg = fmaf(x[mb][e], sl2, -lse2);
+          if constexpr (decltype(masked)::value) {
+            const int key = 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+            arg = lt.vis(own, key) ? arg : -INFINITY;
+          }
+          const float p = fast_exp2(arg);
+          x[mb][e] = p;
+          sum = fmaf(p, y[mb][e], sum);
+        }
+      return sum;
+    });
     dsum += xor32(dsum);
     if (gq == 0) sD[own] = dsum;
 #pragma unroll
@@ -239,16 +250,20 @@ __global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int 
         y[qt] = mfma32<E>(lds_row8<D, E>(sG, 32 * qt, lane & 31, kc, gq), lds_row8<D, E>(sV, 0, own, kc, gq),
                        y[qt]);
       }
+      with_mask(!full, [&](auto masked) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[32 * qt + 8 * i + 4 * gq]);
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[32 * qt + 8 * i + 4 * gq]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * i + j;
-          const bool vis = full || lt.vis(32 * qt + 8 * i + 4 * gq + j, own);
-          x[qt][e] = vis ? fast_exp2(fmaf(x[qt][e], sl2, -L4[j])) : 0.f;
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * i + j;
+            float arg = fmaf(x[qt][e], sl2, -L4[j]);
+            if constexpr (decltype(masked)::value)
+              arg = lt.vis(32 * qt + 8 * i + 4 * gq + j, own) ? arg : -INFINITY;
+            x[qt][e] = fast_exp2(arg);
+          }
         }
-      }
+      });
       // dV^T += dO^T P over this tile's 32 query rows
 #pragma unroll
       for (int c = 0; c < 2; ++c) {

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -82,6 +84,16 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Masked and unmasked instances of a per-tile loop: f(std::true_type{}) when
+// `masked`, else f(std::false_type{}).  The tile-level test is one uniform
+// branch; the masked instance tests every element without branches (bitwise
+// tests and selects) and the unmasked one has no per-element test at all.
+template <typename F>
+__device__ __forceinline__ auto with_mask(bool masked, F&& f) {
+  if (masked) return f(std::true_type{});
+  return f(std::false_type{});
+}
 
 // Wave index within the workgroup, marked wave-uniform: everything derived
 // from it (the wave's rows or keys, tile visibility, skip decisions) then
