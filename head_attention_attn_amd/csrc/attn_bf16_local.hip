@@ -155,8 +155,11 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
 
 // QR: query buffer rows; waves 0-1 own the tile's keys, the QR / 32 waves
 // after them its query rows
+// Three waves per SIMD (three workgroups per CU, which the LDS allows at
+// d <= 96): the register budget that gives measured 7% over the compiler's
+// own choice of two waves per SIMD.
 template <typename E, int D, int QR, bool SR>
-__global__ __launch_bounds__(128 + 2 * QR) void bwd_local_kernel(BwdArgs a, int ntile, int lw, int lq) {
+__global__ __launch_bounds__(128 + 2 * QR) __attribute__((amdgpu_waves_per_eu(3))) void bwd_local_kernel(BwdArgs a, int ntile, int lw, int lq) {
   using V8 = typename E::v8;
   constexpr int NT = 128 + 2 * QR, KE = tile_elems<kTile, D>(), QE = tile_elems<QR, D>();
   constexpr int KC = D / 16, DB = D / 32, QB = QR / 32;

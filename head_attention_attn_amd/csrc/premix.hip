@@ -94,7 +94,10 @@ __device__ __forceinline__ RowMap hp_rows(int N, int lp, int D) {
 template <typename E, int D>
 __global__ __launch_bounds__(2 * D) void premix_fwd_kernel(PremixArgs a) {
   constexpr int NT = 2 * D, XE = tile_elems<32, D>(), SE = tile_elems<kMaxHP, D>();
-  __shared__ __attribute__((aligned(16))) uint16_t sX[XE];
+  // X rows of two positions: the next one streams in (direct-to-LDS) while
+  // the current one is computed; named buffers, two positions per loop trip
+  __shared__ __attribute__((aligned(16))) uint16_t sX0[XE];
+  __shared__ __attribute__((aligned(16))) uint16_t sX1[XE];
   __shared__ __attribute__((aligned(16))) uint16_t sS[SE];  // output staging, rows (h,p)
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);  // this wave's 32 features: 32 * wave ..
@@ -109,11 +112,13 @@ __global__ __launch_bounds__(2 * D) void premix_fwd_kernel(PremixArgs a) {
 
   const RowMap plain{};  // contiguous rows (unused by the SR = false helpers)
   const RowMap rout = hp_rows(a.N, a.lp, D);
-  const int64_t npos = (int64_t)a.B * a.N;
-  for (int64_t pos = blockIdx.x; pos < npos; pos += gridDim.x) {
+  const int64_t npos = (int64_t)a.B * a.N, G = gridDim.x;
+  auto fetch = [&](int64_t pos, uint16_t* x_l) {
+    dma_tile<32, D, NT, false>(x_l, (const uint16_t*)a.x + pos * H * D, plain, 0, H, tid);
+  };
+  // one position from x_l: outputs through sS to global
+  auto position = [&](int64_t pos, const uint16_t* x_l) {
     const int b = (int)(pos / a.N), n = (int)(pos % a.N);
-    dma_tile<32, D, NT, false>(sX, (const uint16_t*)a.x + pos * H * D, plain, 0, H, tid);
-    __syncthreads();
 #pragma unroll
     for (int nt = 0; nt < kMaxHP / 32; ++nt) {
       if (nt >= ntile) break;
@@ -121,17 +126,31 @@ __global__ __launch_bounds__(2 * D) void premix_fwd_kernel(PremixArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         if (16 * ks < H)
-          acc = mfma32<E>(lds_tr8<D, E>(sX, 16 * ks, 32 * wave, lane), wop[nt][ks], acc);
+          acc = mfma32<E>(lds_tr8<D, E>(x_l, 16 * ks, 32 * wave, lane), wop[nt][ks], acc);
       // C[feature 32 wave + 8 i + 4 gq + j][(h,p) 32 nt + lane % 32]
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint2*>(sS + toff2<D>(32 * nt, lane & 31, 32 * wave, 8 * i + 4 * gq)) =
             pack4<E>(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
     }
-    __syncthreads();
+    __syncthreads();  // staging complete (and the prefetch landed)
     uint16_t* out = (uint16_t*)a.out + ((int64_t)b * H * a.N + n) * ((int64_t)D << a.lp);
     store_tile<kMaxHP, D, NT, true>(out, rout, 0, HP, sS, tid);
-    __syncthreads();
+  };
+
+  int64_t pos = blockIdx.x;
+  fetch(pos, sX0);
+  for (;;) {
+    __syncthreads();  // X of pos in sX0; sX1 and sS free
+    if (pos + G < npos) fetch(pos + G, sX1);
+    position(pos, sX0);
+    pos += G;
+    if (pos >= npos) break;
+    __syncthreads();  // X of pos in sX1; sX0 and sS free
+    if (pos + G < npos) fetch(pos + G, sX0);
+    position(pos, sX1);
+    pos += G;
+    if (pos >= npos) break;
   }
 }
 
