@@ -525,14 +525,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
           }
         });
       }
-      // P in register order; dS as a plain [key][query] 32 x 32 tile
+      // P in register order; dS as a [key][query] 32 x 32 tile (ds_tile_off)
       uint16_t* dt = d_l + kb * 1024;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         *reinterpret_cast<V8*>(p_l + hoff + c * 512) = acc_chunk<E>(s, c);
         const V8 v = acc_chunk<E>(dp, c);
-        *reinterpret_cast<V4*>(dt + (lane & 31) * 32 + 16 * c + 4 * gq) = V4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<V4*>(dt + (lane & 31) * 32 + 16 * c + 8 + 4 * gq) =
+        *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + gq)) = V4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) =
             V4{v[4], v[5], v[6], v[7]};
       }
     };
@@ -590,14 +590,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
           *reinterpret_cast<V8*>(blk + (cc * 64 + lane) * 8) =
-              lds_tr8_plain<E>(d_l + kb * 1024, 32, 16 * cc, 0, lane);
+              lds_tr8_ds<E>(d_l + kb * 1024, 16 * cc, 0, lane);
       }
-      const uint16_t* dt = d_l + kb * 1024 + (lane & 31) * 32;
+      const uint16_t* dt = d_l + kb * 1024;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const V8 pop = *reinterpret_cast<const V8*>(p_l + hoff + c * 512);
-        const V4 d0 = *reinterpret_cast<const V4*>(dt + 16 * c + 4 * gq);
-        const V4 d1 = *reinterpret_cast<const V4*>(dt + 16 * c + 8 + 4 * gq);
+        const V4 d0 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * c + gq));
+        const V4 d1 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * c + 2 + gq));
         const V8 dsop = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) {

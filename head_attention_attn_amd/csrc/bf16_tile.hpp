@@ -127,18 +127,25 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, con
   }
 }
 
-// Transposed operand read of a plain row-major tile (row stride `stride`
-// elements, no swizzle): as lds_tr8 -- free index = column c0 + lane % 32,
-// contraction slots = rows r0 + 4g + e, r0 + 8 + 4g + e.
+// The 32 x 32 dS staging tile of the dK/dV pass: row stride 32 elements,
+// 8-byte chunk k of row r stored at chunk position k ^ ((r / 4) % 8).  A
+// column of 8-byte pieces (32 rows, one chunk) then covers all 64 banks, and
+// the transposed reads (4 consecutive rows x 4 chunks per 16 lanes) stay
+// conflict-free; with a plain 64-byte stride the column accesses were 8-way
+// conflicts (measured with SQ_LDS_BANK_CONFLICT).  Element offset of
+// (row r, chunk k).
+__device__ __forceinline__ int ds_tile_off(int r, int k) { return r * 32 + 4 * (k ^ ((r >> 2) & 7)); }
+
+// Transposed operand read of the dS staging tile, as lds_tr8: free index =
+// column c0 + lane % 32, contraction slots = rows r0 + 4g + e, r0 + 8 + 4g + e.
 template <typename E>
-__device__ __forceinline__ typename E::v8 lds_tr8_plain(const uint16_t* tile, int stride, int r0, int c0,
-                                                int lane) {
+__device__ __forceinline__ typename E::v8 lds_tr8_ds(const uint16_t* tile, int r0, int c0, int lane) {
   const int grp = lane >> 4, li = lane & 15;
   const int e = li >> 2, r = li & 3;
   const int g = grp >> 1, half = grp & 1;
-  const uint16_t* p = tile + (r0 + 4 * g + e) * stride + c0 + 16 * half + 4 * r;
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * stride));
+  const int row = r0 + 4 * g + e, k = (c0 >> 2) + 4 * half + r;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + ds_tile_off(row, k)));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + ds_tile_off(row + 8, k)));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(typename E::v8, w);
