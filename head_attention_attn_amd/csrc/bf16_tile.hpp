@@ -243,7 +243,14 @@ __device__ __forceinline__ void acc_to_lds(uint16_t* tile, int row, const f32x16
 // LDS -> global copy of a ROWS x D tile to rows r0 .. of the n rows of a
 // slice (slice base `dst`, rows addressed through `rm`) by NT threads, 16
 // bytes per lane per step, consecutive lanes on consecutive addresses of a
-// row; rows >= n are not written.
+// row; rows >= n are not written.  The stores are non-temporal: every output
+// tile is written once and not read back by the kernel that writes it, and
+// streaming it past the caches keeps the dirty lines of one kernel's outputs
+// from being written back while the next kernel streams its inputs (measured
+// on MI355X: Hiera mask-unit forward 71 -> 52 us when run after the backward,
+// fused backward 103 -> 96 us).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <int ROWS, int D, int NT, bool SR>
 __device__ __forceinline__ void store_tile(uint16_t* dst, const RowMap& rm, int r0, int n,
                                            const uint16_t* lds, int tid) {
@@ -253,9 +260,9 @@ __device__ __forceinline__ void store_tile(uint16_t* dst, const RowMap& rm, int 
     const int c = tid + t * NT;
     const int row = c / CPR, col = (c % CPR) * 8;
     if (c < TOTAL && r0 + row < n)
-      *reinterpret_cast<uint4*>(dst + (SR ? (int64_t)rm.row(r0 + row) : (int64_t)(r0 + row) * D) +
-                                col) =
-          *reinterpret_cast<const uint4*>(lds + toff<D>(row, col));
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(lds + toff<D>(row, col)),
+          reinterpret_cast<u32x4*>(dst + (SR ? (int64_t)rm.row(r0 + row) : (int64_t)(r0 + row) * D) + col));
   }
 }
 
