@@ -35,6 +35,8 @@ namespace {
 
 // ------------------------------------------------------------------ forward
 
+constexpr float kSlack = 8.f;  // log2 of the largest unnormalised P
+
 template <typename E, int D, int NW, int MODE, bool SR>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdArgs a, int nqt) {
   using V8 = typename E::v8;
@@ -97,14 +99,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int kc = 0; kc < KC; ++kc)
         s[mb] = mfma32<E>(lds_row8<D, E>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
     }
-    // (per-element masking under a uniform test of `full`; hoisting that test
-    // out of the loop or masking branch-free measured 5% and 23% slower here)
+    // scaled scores relative to the running max m (log2 units), masked
+    // entries -inf.  (per-element masking under a uniform test of `full`;
+    // hoisting that test out of the loop or masking branch-free measured 5%
+    // and 23% slower here)
+    const float meff = m == -INFINITY ? 0.f : m;
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float x = s[mb][e] * sl2;
+        float x = fmaf(s[mb][e], sl2, -meff);
         if (!full) {
           const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
           if (key < rlo || key >= rhi) x = -INFINITY;
@@ -113,23 +118,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         mx = fmaxf(mx, x);
       }
     mx = fmaxf(mx, xor32(mx));
-    const float mnew = fmaxf(m, mx);
-    const float mu = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m - mu);
+    // m moves only when a row's first visible score arrives or its scores
+    // exceed m by more than 2^kSlack; otherwise P = 2^x stays below 2^kSlack
+    // and O, l keep their scale.  One wave-uniform test per tile.
+    const bool need = m == -INFINITY ? mx > -INFINITY : mx > kSlack;
+    if (__any(need)) {
+      const float sh = need ? mx : 0.f;
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(-sh);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[mb][e] -= sh;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      if (need) m = meff + sh;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(s[mb][e] - mu);
+        const float p = fast_exp2(s[mb][e]);
         s[mb][e] = p;
         rs += p;
       }
     rs += xor32(rs);
-    l = l * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    l += rs;
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c) {
       const V8 pop = acc_chunk<E>(s[c >> 1], c & 1);
