@@ -105,19 +105,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // and 23% slower here)
     const float meff = m == -INFINITY ? 0.f : m;
     float mx = -INFINITY;
+    with_mask(!full, [&](auto masked) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = fmaf(s[mb][e], sl2, -meff);
-        if (!full) {
-          const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
-          if (key < rlo || key >= rhi) x = -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          float x = fmaf(s[mb][e], sl2, -meff);
+          if constexpr (decltype(masked)::value) {
+            const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
+            x = (key >= rlo) & (key < rhi) ? x : -INFINITY;
+          }
+          s[mb][e] = x;
+          mx = fmaxf(mx, x);
         }
-        s[mb][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, xor32(mx));
+    });
+    mx = max_halves(mx);
     // m moves only when a row's first visible score arrives or its scores
     // exceed m by more than 2^kSlack; otherwise P = 2^x stays below 2^kSlack
     // and O, l keep their scale.  One wave-uniform test per tile.
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         s[mb][e] = p;
         rs += p;
       }
-    rs += xor32(rs);
+    rs = sum_halves(rs);
     l += rs;
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c) {

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
       s[mb][e] = x;
       mx = fmaxf(mx, x);
     }
-  mx = fmaxf(mx, xor32(mx));
+  mx = max_halves(mx);
   const float mb2 = qvalid ? mx : 0.f;  // row max of the scaled scores, log2 units
   float l = 0.f;
 #pragma unroll
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
       s[mb][e] = p;
       l += p;
     }
-  l += xor32(l);
+  l = sum_halves(l);
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(128 + 2 * QR) __attribute__((amdgpu_waves_per_eu(3)
         }
       return sum;
     });
-    dsum += xor32(dsum);
+    dsum = sum_halves(dsum);
     if (gq == 0) sD[own] = dsum;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)

@@ -85,6 +85,19 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// x on lane l combined with x on lane l ^ 32 (the same row's other half in
+// the MFMA accumulator layout).  v_permlane32_swap of x with itself leaves
+// the lower-half value in one result and the upper-half value in the other
+// on every lane, with no LDS round trip.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Masked and unmasked instances of a per-tile loop: f(std::true_type{}) when
 // `masked`, else f(std::false_type{}).  The tile-level test is one uniform
 // branch; the masked instance tests every element without branches (bitwise
