@@ -517,17 +517,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       if (!sees(j)) return;
       const int i0 = t0 + j * BQ;
       const bool full = wk1 == wk0 + 32 && mg.tile_full(i0, i0 + BQ, wk0, wk1);
+      // S first, then dP: P = exp2(...) depends on S only and overlaps the
+      // dP products still in the matrix pipe
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        s = mfma32<E>(lds_row8<D, E>(q_l, 0, lane & 31, kc, gq), kop[kc], s);
-        dp = mfma32<E>(lds_row8<D, E>(g_l, 0, lane & 31, kc, gq), vop[kc], dp);
-      }
+      for (int kc = 0; kc < KC; ++kc) s = mfma32<E>(lds_row8<D, E>(q_l, 0, lane & 31, kc, gq), kop[kc], s);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 L4 = *reinterpret_cast<const f32x4*>(&s_l[8 * i + 4 * gq]);
-        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&s_l[32 + 8 * i + 4 * gq]);
-        with_mask(!full, [&](auto masked) {
+      for (int kc = 0; kc < KC; ++kc) dp = mfma32<E>(lds_row8<D, E>(g_l, 0, lane & 31, kc, gq), vop[kc], dp);
+      with_mask(!full, [&](auto masked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&s_l[8 * i + 4 * gq]);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int e = 4 * i + jj;
@@ -536,11 +536,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
               const int qi = i0 + 8 * i + 4 * gq + jj;
               arg = ((qi >= clo) & (qi < chi)) ? arg : -INFINITY;
             }
-            const float p = fast_exp2(arg);
-            s[e] = p;
-            dp[e] = p * (dp[e] - D4[jj]);
+            s[e] = fast_exp2(arg);
           }
-        });
+        }
+      });
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&s_l[32 + 8 * i + 4 * gq]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dp[4 * i + jj] = s[4 * i + jj] * (dp[4 * i + jj] - D4[jj]);
       }
       // P in register order; dS as a [key][query] 32 x 32 tile (ds_tile_off)
       uint16_t* dt = d_l + kb * 1024;
