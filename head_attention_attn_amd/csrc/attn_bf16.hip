@@ -603,15 +603,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       if (!sees(j)) return;
       if (a.ds) {
         // keep the block for the dQ pass, already in its MFMA operand order
-        // (lane = query, 8 keys of a 16-key chunk per lane): 2 x 1 KB.  Block
+        // (lane = query, 8 keys of a 16-key chunk per lane): 2 x 1 KB,
+        // streamed past the caches like the output tiles.  Block
         // i0 / 32 - wlo / 32 of this key block's ds_count(): in range because
         // sees(j) holds (a nonempty query range overlapping the tile).
         const int i0 = t0 + j * BQ;
         uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
-          *reinterpret_cast<V8*>(blk + (cc * 64 + lane) * 8) =
-              lds_tr8_ds<E>(d_l + kb * 1024, 16 * cc, 0, lane);
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, lds_tr8_ds<E>(d_l + kb * 1024, 16 * cc, 0, lane)),
+                                      reinterpret_cast<u32x4*>(blk + (cc * 64 + lane) * 8));
       }
       const uint16_t* dt = d_l + kb * 1024;
 #pragma unroll
