@@ -186,14 +186,20 @@ def iha_setup(attn, torch, w, dev):
 
 def premix_parity(iha, w, npos: int = 32):
     """The first ``npos`` positions of the Q premix against the oracle:
-    max |gpu - ref| / (2^-8 |ref| + 1e-6), the bf16 output-rounding bound."""
+    max |gpu - ref| / bound.  The fp32 sum s of H products is within
+    H 2^-24 sum|terms| of ref, and rounding it to bf16 adds at most 2^-8 |s|
+    <= 2^-8 (|ref| + |s - ref|), so the bound is
+    2^-8 |ref| + (1 + 2^-8) H 2^-24 sum|terms|."""
     import numpy as np
     from oracle.premix import premix_fwd
     x = iha["x"][0][:, :npos].double().cpu().numpy()
     wt = iha["w"][0].double().cpu().numpy()
     ref = premix_fwd(x, wt)
+    absref = premix_fwd(np.abs(x), np.abs(wt))
     got = iha["out"][0][:, :, :npos].double().cpu().numpy()
-    return float(np.max(np.abs(got - ref) / (2.0 ** -8 * np.abs(ref) + 1e-6)))
+    u = 2.0 ** -8
+    bound = u * np.abs(ref) + (1 + u) * w.H * 2.0 ** -24 * absref + 1e-30
+    return float(np.max(np.abs(got - ref) / bound))
 
 
 # ------------------------------------------------------- Hiera token order

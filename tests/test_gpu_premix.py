@@ -3,9 +3,11 @@ against the fp64 oracle (oracle/premix.py) on the same seeded inputs, and of
 the whole interleaved-head-attention chain (premix of Q, K, V -> sliding
 window attention over the pseudo-tokens -> backward through both).
 
-Bounds, element by element, from the arithmetic: a 16-bit output rounded to
-nearest even from an fp32 sum of n products is within u |ref| + n 2^-24
-sum |terms| of the exact value (u = 2^-8 for bf16, 2^-11 for fp16); dW is fp32
+Bounds, element by element, from the arithmetic: the fp32 sum s of n
+products is within n 2^-24 sum |terms| of the exact value ref, and rounding
+s to nearest even in 16 bits adds at most u |s| <= u (|ref| + |s - ref|), so
+the output is within u |ref| + (1 + u) n 2^-24 sum |terms| of ref (u = 2^-8
+for bf16, 2^-11 for fp16); dW is fp32
 (a blocked sum over B * N * d products): within depth * 2^-24 sum |terms|, with
 depth the longest chain of additions of the blocking (``dw_depth``).  In the chained test the gradients reaching
 the inputs are products of the attention gradients (bf16 tolerance) and W,
@@ -29,7 +31,7 @@ U = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
 
 
 def check_elementwise(name, got, ref, absref, u, nterms):
-    bound = u * np.abs(ref) + (nterms * 2.0 ** -24 + 1e-30) * absref + 1e-7
+    bound = u * np.abs(ref) + (1 + u) * (nterms * 2.0 ** -24 + 1e-30) * absref + 1e-7
     err = np.abs(got - ref)
     worst = float(np.max(err / bound))
     assert worst <= 1.0, f"{name}: error {worst:.2f} x its bound"
