@@ -53,10 +53,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // longest causal rows first
   MaskGeom mg = a.mg;
   if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
+  // longest causal rows first
+  const TileId tix = tile_of(blockIdx.x, BH, nqt, mg.mode == kCausal, true);
+  const int bh = tix.bh, qt = tix.t;
   const int i0 = qt * BM, i1 = min(i0 + BM, a.nq);
 
   const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
@@ -249,10 +250,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int kt = (int)(blockIdx.x / BH);  // causal: low key tiles see the most queries
   MaskGeom mg = a.mg;
   if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
+  // causal: low key tiles see the most queries
+  const TileId tix = tile_of(blockIdx.x, BH, nkt, mg.mode == kCausal, false);
+  const int bh = tix.bh, kt = tix.t;
   const int k0 = kt * BK, k1 = min(k0 + BK, a.nk);
 
   const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
@@ -442,10 +444,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int kt = (int)(blockIdx.x / BH);  // causal: low key tiles see the most queries
   MaskGeom mg = a.mg;
   if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
+  // causal: low key tiles see the most queries
+  const TileId tix = tile_of(blockIdx.x, BH, nkt, mg.mode == kCausal, false);
+  const int bh = tix.bh, kt = tix.t;
   const int k0 = kt * BK, k1 = min(k0 + BK, a.nk);
   const int kb = wave & 3;                 // key block of this wave (either role)
   const int wk0 = k0 + 32 * kb, wk1 = min(wk0 + 32, a.nk);
@@ -681,10 +684,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
   MaskGeom mg = a.mg;
   if (MODE != kAnyMask) mg.mode = MODE;
+  // longest causal rows first
+  const TileId tix = tile_of(blockIdx.x, BH, nqt, mg.mode == kCausal, true);
+  const int bh = tix.bh, qt = tix.t;
   const int i0 = qt * BM, i1 = min(i0 + BM, a.nq);
   const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
   const uint16_t* DS = a.ds + (int64_t)bh * a.ds_per_bh * kDsBlockElems;
@@ -776,10 +780,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int qt = nqt - 1 - (int)(blockIdx.x / BH);
   MaskGeom mg = a.mg;
   if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
+  // longest causal rows first
+  const TileId tix = tile_of(blockIdx.x, BH, nqt, mg.mode == kCausal, true);
+  const int bh = tix.bh, qt = tix.t;
   const int i0 = qt * BM, i1 = min(i0 + BM, a.nq);
 
   const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
