@@ -92,13 +92,17 @@ __device__ __forceinline__ RowMap hp_rows(int N, int lp, int D) {
 }
 
 template <typename E, int D>
-__global__ __launch_bounds__(2 * D) void premix_fwd_kernel(PremixArgs a) {
-  constexpr int NT = 2 * D, XE = tile_elems<32, D>(), SE = tile_elems<kMaxHP, D>();
+__global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(4))) void premix_fwd_kernel(PremixArgs a) {
+  constexpr int NT = 2 * D, XE = tile_elems<32, D>();
   // X rows of two positions: the next one streams in (direct-to-LDS) while
-  // the current one is computed; named buffers, two positions per loop trip
+  // the current one is computed; named buffers, two positions per loop trip.
+  // Outputs are staged 32 rows (h,p) at a time in two alternating buffers,
+  // so a tile is computed while the previous one is being stored: 4 tiles
+  // of LDS in all, four workgroups per CU.
   __shared__ __attribute__((aligned(16))) uint16_t sX0[XE];
   __shared__ __attribute__((aligned(16))) uint16_t sX1[XE];
-  __shared__ __attribute__((aligned(16))) uint16_t sS[SE];  // output staging, rows (h,p)
+  __shared__ __attribute__((aligned(16))) uint16_t sS0[XE];
+  __shared__ __attribute__((aligned(16))) uint16_t sS1[XE];
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
   const int wave = wave_id(tid);  // this wave's 32 features: 32 * wave ..
   const int H = a.H, HP = a.H << a.lp, ntile = (HP + 31) / 32;
@@ -116,12 +120,17 @@ __global__ __launch_bounds__(2 * D) void premix_fwd_kernel(PremixArgs a) {
   auto fetch = [&](int64_t pos, uint16_t* x_l) {
     dma_tile<32, D, NT, false>(x_l, (const uint16_t*)a.x + pos * H * D, plain, 0, H, tid);
   };
-  // one position from x_l: outputs through sS to global
+  // one position from x_l: outputs through sS0 / sS1 to global.  Tile nt
+  // is written into the buffer tile nt - 2 was stored from; every thread is
+  // past that store since it passed the barrier of tile nt - 1 (the first
+  // tile of a position follows the position's own barrier).
   auto position = [&](int64_t pos, const uint16_t* x_l) {
     const int b = (int)(pos / a.N), n = (int)(pos % a.N);
+    uint16_t* out = (uint16_t*)a.out + ((int64_t)b * H * a.N + n) * ((int64_t)D << a.lp);
 #pragma unroll
     for (int nt = 0; nt < kMaxHP / 32; ++nt) {
       if (nt >= ntile) break;
+      uint16_t* st = (nt & 1) ? sS1 : sS0;
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -130,12 +139,11 @@ __global__ __launch_bounds__(2 * D) void premix_fwd_kernel(PremixArgs a) {
       // C[feature 32 wave + 8 i + 4 gq + j][(h,p) 32 nt + lane % 32]
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint2*>(sS + toff2<D>(32 * nt, lane & 31, 32 * wave, 8 * i + 4 * gq)) =
+        *reinterpret_cast<uint2*>(st + toff2<D>(0, lane & 31, 32 * wave, 8 * i + 4 * gq)) =
             pack4<E>(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+      __syncthreads();  // staging complete (and, at nt = 0, the prefetch landed)
+      store_tile<32, D, NT, true>(out, rout, 32 * nt, HP, st, tid);
     }
-    __syncthreads();  // staging complete (and the prefetch landed)
-    uint16_t* out = (uint16_t*)a.out + ((int64_t)b * H * a.N + n) * ((int64_t)D << a.lp);
-    store_tile<kMaxHP, D, NT, true>(out, rout, 0, HP, sS, tid);
   };
 
   int64_t pos = blockIdx.x;
