@@ -248,8 +248,12 @@ __global__ __launch_bounds__(1024) void premix_dw_reduce_kernel(const float* __r
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
   float acc = 0.f;
-  if (e < nelem)
+  // (unrolled so that the loads of several partials are in flight at once;
+  // the additions keep their order)
+  if (e < nelem) {
+#pragma unroll 16
     for (int g = wave; g < nparts; g += 16) acc += part[(int64_t)g * nelem + e];
+  }
   sP[wave][lane] = acc;
   __syncthreads();
   if (wave == 0 && e < nelem) {
