@@ -234,6 +234,26 @@ inline bool rows_plain(const BwdArgs& a, int d) {
          a.rdk.plain(a.H, a.nk, d) && a.rdv.plain(a.H, a.nk, d);
 }
 
+// The (b, h) slice and tile index of workgroup L of a BH x nt grid.  Tiles
+// are taken heaviest first (`first_heavy`: query tile nt - 1 first when true,
+// key tile 0 first when false; causal and sliding masks give the late query
+// tiles / early key tiles the most work).  Under a causal mask the grid keeps
+// one tile index across all slices at a time, for load balance.  Other masks
+// lay the workgroups out XCD by XCD: the dispatcher sends workgroup L to XCD
+// L % 8, and XCD x takes the contiguous run of (slice, tile) items starting
+// at x q + min(x, r) (BH nt = 8 q + r), tiles of a slice adjacent, so tiles
+// that read the same K/V (or Q/dO) rows run on one XCD and share its L2.
+struct TileId {
+  int bh, t;
+};
+ATTN_HD TileId tile_of(int L, int BH, int nt, bool causal, bool first_heavy) {
+  if (causal) return {L % BH, first_heavy ? nt - 1 - L / BH : L / BH};
+  const int x = L & 7, T = BH * nt, q = T >> 3, r = T & 7;
+  const int item = x * q + (x < r ? x : r) + (L >> 3);
+  const int t = item % nt;
+  return {item / nt, first_heavy ? nt - 1 - t : t};
+}
+
 // backward pass bits (the values of include/attn.h's ATTN_PASS_*)
 enum BwdPass : int { kPassRowSum = 1, kPassDKDV = 2, kPassDQ = 4, kPassAll = 7 };
 

@@ -2,6 +2,7 @@
 // attn_common.hpp (host build, no GPU).  Exit status 0 iff every check holds.
 #include <cstdio>
 #include <cstdlib>
+#include <vector>
 
 #include "attn_common.hpp"
 
@@ -108,7 +109,40 @@ static void check(int mode, int W, int nq, int nk) {
   }
 }
 
+// workgroup -> (slice, tile) order of the general kernels: every (slice,
+// tile) pair exactly once; causal grids keep one tile index across all
+// slices at a time, heaviest first; other grids give each XCD (workgroup
+// L -> XCD L % 8) one contiguous run of items, tiles of a slice adjacent
+static void check_tile_order(int BH, int nt) {
+  const int T = BH * nt;
+  for (int causal = 0; causal < 2; ++causal)
+    for (int heavy = 0; heavy < 2; ++heavy) {
+      std::vector<int> seen(T, 0);
+      for (int L = 0; L < T; ++L) {
+        const attn::TileId t = attn::tile_of(L, BH, nt, causal, heavy);
+        CHECK(t.bh >= 0 && t.bh < BH && t.t >= 0 && t.t < nt, "tile_of out of range BH%d nt%d L%d\n", BH, nt, L);
+        if (t.bh >= 0 && t.bh < BH && t.t >= 0 && t.t < nt) ++seen[t.bh * nt + t.t];
+        if (causal) {
+          CHECK(t.bh == L % BH && t.t == (heavy ? nt - 1 - L / BH : L / BH), "causal order BH%d nt%d L%d\n", BH,
+                nt, L);
+        } else if (L >= 8) {
+          // the previous workgroup of the same XCD took the preceding item
+          const attn::TileId p = attn::tile_of(L - 8, BH, nt, causal, heavy);
+          const int item = t.bh * nt + (heavy ? nt - 1 - t.t : t.t);
+          const int prev = p.bh * nt + (heavy ? nt - 1 - p.t : p.t);
+          CHECK(item == prev + 1, "XCD run not contiguous BH%d nt%d L%d\n", BH, nt, L);
+        }
+      }
+      for (int e = 0; e < T; ++e) CHECK(seen[e] == 1, "tile_of not a bijection BH%d nt%d item%d\n", BH, nt, e);
+    }
+}
+
 int main() {
+  const int bhs[] = {1, 3, 8, 20, 80, 512};
+  const int nts[] = {1, 2, 7, 32, 64};
+  for (int bh : bhs)
+    for (int nt : nts) check_tile_order(bh, nt);
+
   const int sizes[] = {1, 2, 4, 5, 16, 17, 33, 64, 65, 96, 128};
   for (int nq : sizes)
     for (int nk : sizes) {
