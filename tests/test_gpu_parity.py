@@ -155,6 +155,34 @@ def test_large_logits_and_key_offset(dtype, d, N, mask, rel_tol, amax_frac):
     compare([("lse", to64(lse), rl)], dtype, "stress lse", tol=(0, 0, 1e-3))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("mask,window", [("causal", 0), ("none", 0), ("sliding", 300)])
+def test_growing_scores_move_the_running_max(dtype, mask, window):
+    """Scores that grow along the keys (about 4 log2 units per 64-key tile,
+    plus one planted key whose scores jump by ~60) make the forward's running
+    max move again and again inside long rows -- the rare path of its online
+    softmax (rescaling O and l when a row's scores exceed the max by more
+    than 2^8) -- and keep unnormalised P values up to 2^8 elsewhere.  O and
+    lse against the oracle within the tolerances of the input type; the
+    softmax weights are smooth (an exponential window of ~24 keys), so the
+    same rounding arguments hold as for N(0, 1) inputs."""
+    B, H, N, d = 1, 2, 1030, 64
+    say(f"[running max] {dtype} {mask} W={window} N={N}")
+    q, k, v, do = make_inputs(B, H, N, N, d, dtype, seed=12)
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    ramp = torch.arange(N, dtype=torch.float32) / N
+    qf, kf = q.float() * 0.1, k.float() * 0.1
+    qf[..., 0] = 16.0
+    kf[..., 0] = 20.8 * ramp                  # scores rise ~0.06 log2 units per key
+    kf[..., 700, 0] += 20.8                   # one key ~60 log2 units above its neighbours
+    q, k = qf.to(q.dtype), kf.to(k.dtype)
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), mask=mask, window=window, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle_fwd(to64(q), to64(k), to64(v), scale, mask, window)
+    rep = compare([("O", to64(o), ro), ("lse", to64(lse), rl)], dtype, f"running max {mask}")
+    say(f"[running max] {rep}")
+
+
 def test_deterministic_bitwise():
     say("[determinism] causal bf16 d=128 N=333")
     q, k, v, do = make_inputs(1, 4, 333, 333, 128, "bf16", seed=7)
