@@ -12,9 +12,11 @@
 // tile is consumed), K is read row-wise and V column-wise with the LDS
 // transpose read.  P^T leaves the score accumulator directly as the bf16
 // operand of the PV contraction (no LDS round trip).  The online softmax runs
-// in base 2 with scale*log2(e) folded into the scores.  Key tiles outside a
-// workgroup's visible range are never loaded; tiles a wave cannot see are
-// skipped by that wave; only tiles that are not fully visible are masked.
+// in base 2 with scale*log2(e) folded into the scores, and its running max
+// moves only when a row's scores exceed it by more than 2^kSlack.  Key tiles
+// outside a workgroup's visible range are never loaded; tiles a wave cannot
+// see are skipped by that wave; only tiles that are not fully visible are
+// masked.  Workgroups take (slice, tile) items in the order of tile_of().
 //
 // Backward ("IHA-CUDA", Repository Structure: preprocess (dPsum, lse), flash
 // backward, postprocess dQaccum -> dQ), restructured as three deterministic

@@ -83,8 +83,6 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
-
 // x on lane l combined with x on lane l ^ 32 (the same row's other half in
 // the MFMA accumulator layout).  v_permlane32_swap of x with itself leaves
 // the lower-half value in one result and the upper-half value in the other
