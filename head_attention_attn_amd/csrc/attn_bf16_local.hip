@@ -71,7 +71,11 @@ template <typename E, int D, int QR, bool SR>
 __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) void fwd_local_kernel(FwdArgs a, int ntile, int lw, int lq) {
   using V8 = typename E::v8;
   constexpr int NT = 2 * QR, TE = tile_elems<kTile, D>(), KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[TE];
+  // with one wave per tile (QR = 32) the K rows go straight into registers:
+  // no wave reads them twice, and half the LDS per tile doubles the tiles
+  // (and bytes) in flight per CU
+  constexpr bool KREG = QR == 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[KREG ? 8 : TE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[TE];
 
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 5;
@@ -85,8 +89,15 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
   const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
   const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
 
-  dma_tile<kTile, D, NT, SR>(sK, K, a.rk, tk0, a.nk, tid);
+  if constexpr (!KREG) dma_tile<kTile, D, NT, SR>(sK, K, a.rk, tk0, a.nk, tid);
   dma_tile<kTile, D, NT, SR>(sV, V, a.rv, tk0, a.nk, tid);
+  V8 kop[KREG ? 2 : 1][KC];
+  if constexpr (KREG) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      load_operand_rows<D, E>(kop[mb], K + rrow<SR, D>(a.rk, min(tk0 + 32 * mb + (lane & 31), a.nk - 1)), true,
+                              gq);
+  }
   const int myr = wave * 32 + (lane & 31);  // this lane's query row in the tile
   const int myq = lt.tq0 + myr;
   const bool qvalid = lt.real(myr);
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
     s[mb] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      s[mb] = mfma32<E>(lds_row8<D, E>(sK, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
+      s[mb] = mfma32<E>(KREG ? kop[mb][kc] : lds_row8<D, E>(sK, mb * 32, lane & 31, kc, gq), qop[kc], s[mb]);
   }
   // one 64-key window of 64 rows, whole: nothing to mask
   const bool full = lw == 6 && lq == 6 && tk0 + kTile <= a.nk;
@@ -141,14 +152,16 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
     for (int db = 0; db < DB; ++db)
       oacc[db] = mfma32<E>(lds_tr8<D, E>(sV, 16 * c, 32 * db, lane), pop, oacc[db]);
   }
-  // O rows through LDS (sK is free once every wave is past its products) so
-  // that the global stores are whole rows, 16 bytes per lane
+  // O rows through LDS (sK, or sV with K in registers, is free once every
+  // wave is past its products) so that the global stores are whole rows, 16
+  // bytes per lane
+  uint16_t* stage = KREG ? sV : sK;
   __syncthreads();
-  acc_to_lds<D, E>(sK, myr, oacc, qvalid ? 1.f / l : 0.f, gq);
+  acc_to_lds<D, E>(stage, myr, oacc, qvalid ? 1.f / l : 0.f, gq);
   if (qvalid && gq == 0) a.lse[(int64_t)bh * a.nq + myq] = (mb2 + log2f(l)) * kLn2;
   __syncthreads();
   uint16_t* O = (uint16_t*)a.o + rslice<SR, D>(a.ro, bh, a.H, a.nq);
-  store_tile<QR, D, NT, SR>(O, a.ro, lt.tq0, lt.qend, sK, tid);
+  store_tile<QR, D, NT, SR>(O, a.ro, lt.tq0, lt.qend, stage, tid);
 }
 
 // ----------------------------------------------------------------- backward
