@@ -199,6 +199,25 @@ def _mask_args(q, mask, window):
     return mask, window
 
 
+def _check_out(t, like, name):
+    """A caller-provided output: on like's device, in like's dtype and shape
+    (its rows may be strided like the inputs')."""
+    if not isinstance(t, torch.Tensor) or t.device != like.device or t.dtype != like.dtype \
+            or tuple(t.shape) != tuple(like.shape):
+        raise ValueError(f"{name} must be a {like.dtype} tensor shaped {tuple(like.shape)} "
+                         f"on {like.device}")
+    return t
+
+
+def _check_lse(t, B, H, Nq, device):
+    """lse: a contiguous float32 [B, H, Nq] device tensor (the library writes
+    B * H * Nq floats at its base)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device \
+            or tuple(t.shape) != (B, H, Nq) or not t.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 tensor [{B}, {H}, {Nq}] on {device}")
+    return t
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -214,10 +233,9 @@ def fwd(q, k, v, mask: str = "none", window: int = 0, scale=None, out=None, lse=
     (o shaped like q, in q.dtype; lse [B, H, Nq] float32)."""
     lib = load_library()
     B, H, Nq, Nk, d, mask, window = _geometry(q, k, v, *_mask_args(q, mask, window))
-    o = _empty_rows(q) if out is None else out
-    if tuple(o.shape) != tuple(q.shape):
-        raise ValueError("out must be shaped like q")
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _empty_rows(q) if out is None else _check_out(out, q, "out")
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None \
+        else _check_lse(lse, B, H, Nq, q.device)
     args = (DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d), MASK_CODES[mask], window,
             q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
     if _is_plain(q, k, v, o):
@@ -266,15 +284,17 @@ def bwd(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
     for the dQ pass to read dS kept by the dK/dV pass, else the minimum."""
     lib = load_library()
     B, H, Nq, Nk, d, mask, window = _geometry(q, k, v, *_mask_args(q, mask, window))
-    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape) \
-            or tuple(lse.shape) != (B, H, Nq):
-        raise ValueError("o/do must match q and lse must be [B, H, Nq]")
+    _check_out(o, q, "o")
+    _check_out(do, q, "do")
+    _check_lse(lse, B, H, Nq, q.device)
     ws_need = workspace_bytes_ds(q, k, mask, window) if keep_ds else workspace_bytes(B, H, Nq)
     if workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
-    dq = _empty_rows(q) if dq is None else dq
-    dk = _empty_rows(k) if dk is None else dk
-    dv = _empty_rows(v) if dv is None else dv
+    dq = _empty_rows(q) if dq is None else _check_out(dq, q, "dq")
+    dk = _empty_rows(k) if dk is None else _check_out(dk, k, "dk")
+    dv = _empty_rows(v) if dv is None else _check_out(dv, v, "dv")
+    if workspace is not None and (workspace.device != q.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     args = (int(passes), DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d),
             MASK_CODES[mask], window, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
             lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
@@ -305,6 +325,12 @@ def _premix_shapes(x, w):
     return B, N, H, w.shape[1], d
 
 
+def _check_contiguous(t, shape, dtype, device, name):
+    if not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype \
+            or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor {list(shape)} on {device}")
+
+
 def premix_workspace_bytes(B: int, N: int, H: int, P: int) -> int:
     return int(load_library().attn_premix_bwd_workspace_size(B, N, H, P))
 
@@ -318,6 +344,7 @@ def premix(x, w, out=None):
     B, N, H, P, d = _premix_shapes(x, w)
     if out is None:
         out = torch.empty((B, H, N, P, d), dtype=x.dtype, device=x.device)
+    _check_contiguous(out, (B, H, N, P, d), x.dtype, x.device, "out")
     st = lib.attn_premix_fwd(DTYPE_CODES[x.dtype], B, N, H, P, d, x.data_ptr(), w.data_ptr(),
                              out.data_ptr(), _stream(x))
     if st != 0:
@@ -334,6 +361,8 @@ def premix_bwd(x, w, dout, dx=None, dw=None, workspace=None):
         raise ValueError("dout must be a contiguous [B, H, N, P, d] tensor of x's dtype")
     dx = torch.empty_like(x) if dx is None else dx
     dw = torch.empty((H, P, H), dtype=torch.float32, device=x.device) if dw is None else dw
+    _check_contiguous(dx, tuple(x.shape), x.dtype, x.device, "dx")
+    _check_contiguous(dw, (H, P, H), torch.float32, x.device, "dw")
     if workspace is None:
         workspace = torch.empty(premix_workspace_bytes(B, N, H, P), dtype=torch.uint8,
                                 device=x.device)

@@ -243,6 +243,30 @@ def test_error_paths_leave_outputs_untouched():
     assert bool((o == 7).all()) and bool((lse == 7).all())
 
 
+def test_binding_rejects_mismatched_outputs():
+    """Caller-provided outputs of the wrong dtype, shape, device or layout are
+    refused before any launch (the library writes B * H * Nq floats at lse's
+    base and whole rows at the others')."""
+    q, k, v, do = (t.cuda() for t in make_inputs(1, 2, 64, 64, 64, "bf16", seed=9))
+    bad = [dict(out=torch.empty(1, 2, 64, 64, device="cuda")),                    # fp32 O
+           dict(out=torch.empty(1, 2, 32, 64, dtype=torch.bfloat16, device="cuda")),
+           dict(lse=torch.empty(1, 2, 32, device="cuda")),                        # short lse
+           dict(lse=torch.empty(1, 2, 64, dtype=torch.float64, device="cuda")),
+           dict(lse=torch.empty(1, 64, 2, device="cuda").transpose(1, 2))]        # strided lse
+    for kw in bad:
+        with pytest.raises(ValueError):
+            attn.fwd(q, k, v, mask="causal", **kw)
+    o, lse = attn.fwd(q, k, v, mask="causal")
+    for kw in (dict(dq=torch.empty(1, 2, 64, 32, dtype=torch.bfloat16, device="cuda")),
+               dict(dk=torch.empty(1, 2, 64, 64, device="cuda")),
+               dict(dv=torch.empty(1, 2, 64, 64, dtype=torch.bfloat16))):
+        with pytest.raises(ValueError):
+            attn.bwd(q, k, v, o, lse, do, mask="causal", **kw)
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, o, lse[:, :, :32], do, mask="causal")
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("window,n", [(64, 192), (32, 96), (16, 208), (8, 40), (4, 12), (2, 130),
                                       (1, 65)])
