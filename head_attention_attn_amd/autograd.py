@@ -24,10 +24,11 @@ class FusedAttentionFunction(torch.autograd.Function):
 
     Inputs: device tensors q [B, H, Nq, d], k and v [B, H, Nk, d] with any
     row strides (views of a projection output need no copy), or window-split
-    [B, nw, H, T, d] views for the block mask (bf16 or fp32); the mask name,
-    its window and the scale (None: d^-0.5).  Returns O shaped like q.  ``keep_ds`` picks the backward workspace: large
-    enough for the dQ pass to read dS kept by the dK/dV pass where that path
-    applies (``attn_bwd_workspace_size_ds``), else the minimum."""
+    [B, nw, H, T, d] views for the block mask (bf16, fp16 or fp32); the mask
+    name, its window and the scale (None: d^-0.5).  Returns O shaped like q.
+    ``keep_ds`` picks the backward workspace: large enough for the dQ pass to
+    read dS kept by the dK/dV pass where that path applies
+    (``attn_bwd_workspace_size_ds``), else the minimum."""
 
     @staticmethod
     def forward(ctx, q, k, v, mask="none", window=0, scale=None, keep_ds=True):
