@@ -71,17 +71,17 @@ size_t ws_size(int64_t B, int64_t H, int64_t Nq) {
 // gfx950 check, cached per device ordinal.
 int check_device() {
   static std::mutex mu;
-  static signed char verdict[64];  // 0 unknown, 1 ok, -1 unsupported
+  static signed char arch_ok[64];  // 0 unknown, 1 ok, -1 unsupported
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
   if (dev >= 64) return ATTN_ERR_DEVICE;
   std::lock_guard<std::mutex> lock(mu);
-  if (verdict[dev] == 0) {
+  if (arch_ok[dev] == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
-    verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
   }
-  return verdict[dev] == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
+  return arch_ok[dev] == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
 attn::MaskGeom make_geom(int mask, int64_t Nq, int64_t Nk, int64_t window) {
