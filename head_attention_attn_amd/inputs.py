@@ -97,6 +97,19 @@ def make_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str = "bf16",
     return q, k, v, do
 
 
+def make_device_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str = "bf16",
+                       seed: int = 0, device: str = "cuda"):
+    """(q, k, v, do) drawn on the device, N(0, 1) in the requested type, from
+    one generator of that device seeded with ``seed``, in that order: for
+    tensors of several GB that the host would take minutes to draw.  The
+    checks compare slices copied back to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tdt = TORCH_DTYPES[dtype]
+    shapes = ((B, H, Nq, d), (B, H, Nk, d), (B, H, Nk, d), (B, H, Nq, d))
+    return tuple(torch.randn(s, dtype=tdt, device=device, generator=g) for s in shapes)
+
+
 def workload_inputs(w: Workload, seed: int = 0):
     return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, seed)
 

@@ -106,7 +106,11 @@ enum attn_status {
  *   dtype        ATTN_BF16, ATTN_FP16 or ATTN_FP32 (element type of q, k, v,
  *                o and of every other tensor but lse)
  *   B, H         batch and head count (>= 1)
- *   Nq, Nk       query and key sequence lengths (>= 1)
+ *   Nq, Nk       query and key sequence lengths (>= 1, <= 2^30; every
+ *                (b, h) slice spans at most 2^31 elements, i.e. Nq * d and
+ *                Nk * d <= 2^31 for contiguous tensors, and
+ *                B * H * ceil(max(Nq, Nk) / 16) < 2^31; ATTN_ERR_INVALID_ARG
+ *                otherwise.  Whole tensors may exceed 2^31 elements.)
  *   d            head dimension: 64, 96 or 128
  *   scale        multiplier of Q K^T (e.g. 1/sqrt(d))
  *   mask, window mask mode and its window (ignored for NONE and CAUSAL)

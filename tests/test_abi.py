@@ -248,3 +248,18 @@ def test_premix_validation(lib):
     assert cb() == OK
     assert cb(wsz=wsz - 1) == WORKSPACE and cb(ws=0) == WORKSPACE
     assert cb(dx=dout) == ALIAS and cb(dw=dx + 16) == ALIAS
+
+
+def test_size_limits(lib):
+    """A (b, h) slice spans at most 2^31 elements (the kernels address rows
+    inside a slice with 32-bit offsets); whole tensors may be larger."""
+    far = [(1 << 44) + i * (1 << 41) for i in range(5)]        # 2 TiB apart: no overlap
+    def chk(B, Nq, Nk, d, mask=0, window=0):
+        q, k, v, o, lse = far
+        return lib.attn_check_fwd(BF16, B, 1, Nq, Nk, d, 0.125, mask, window, q, k, v, o, lse)
+    assert chk(1, 1 << 25, 1 << 25, 64) == OK                 # Nq * d = 2^31 exactly
+    assert chk(1, (1 << 25) + 1, 64, 64) == INVALID           # query slice past 2^31
+    assert chk(1, 64, (1 << 25) + 1, 64) == INVALID           # key slice past 2^31
+    assert chk(1, (1 << 24) + 16, 64, 128) == INVALID         # d = 128: 2^24 rows is the bound
+    assert chk(4, 1 << 24, 1 << 24, 64, mask=2, window=64) == OK   # 2^32 elements per tensor
+    assert chk(1, (1 << 30) + 1, 64, 64) == INVALID           # row count past 2^30
