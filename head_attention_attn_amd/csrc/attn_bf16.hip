@@ -412,7 +412,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
 //     operands; per 32-query tile S = Q K^T, dP = dO V^T, P = exp(S*scale -
 //     lse), dS = P (dP - D), rounded to bf16 and handed over through LDS (P in
 //     the accumulator's register order, 16 bytes per lane per 16-row chunk;
-//     dS as a plain [key][query] tile);
+//     dS as a [key][query] tile, 8-byte chunks swizzled by ds_tile_off);
 //   accumulate waves 4..7 (key block w - 4): dV^T += dO^T P, dK^T += Q^T dS
 //     with dO^T, Q^T from transpose reads of the same Q / dO tiles; when the
 //     caller gave room they also write each dS tile to the workspace for the

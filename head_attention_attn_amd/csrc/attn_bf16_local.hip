@@ -11,11 +11,13 @@
 // around moving each byte once.
 //
 // Forward: one workgroup per tile, one wave per 32 query rows (QR = 32 or 64
-// rows of query buffer, QT of them real).  K and V of the tile go to LDS,
-// each wave keeps 32 query rows as the register operand, and the scores of a
-// row are complete after one tile, so the softmax is a plain one (exact row
-// max, no rescaling).  Computed transposed like the general forward kernel:
-// S^T = K Q^T, O^T = V^T P^T with bf16 MFMA 32x32x16.
+// rows of query buffer, QT of them real).  V of the tile goes to LDS, and K
+// too when two waves share it (with one wave, QR = 32, K goes straight into
+// the wave's operand registers); each wave keeps 32 query rows as the
+// register operand, and the scores of a row are complete after one tile, so
+// the softmax is a plain one (exact row max, no rescaling).  Computed
+// transposed like the general forward kernel: S^T = K Q^T, O^T = V^T P^T
+// with bf16 MFMA 32x32x16.
 //
 // Backward: one workgroup per tile, Q, K, V and dO staged in LDS once.  The
 // dK/dV pass and the dQ pass ("IHA-CUDA", Repository Structure: separate
