@@ -351,6 +351,8 @@ def main() -> int:
                     help="run a 16-bit workload in this element type instead")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline (0 skips it)")
+    ap.add_argument("--graph-steps", type=int, default=20,
+                    help="steps replayed from the step captured in a HIP graph (0: skip)")
     ap.add_argument("--autograd-steps", type=int, default=20,
                     help="after the timed region, time this many steps through the "
                          "torch.autograd wrapper (0 skips it)")
@@ -488,6 +490,29 @@ def main() -> int:
         log(f"[bench] autograd wrapper: {ag_ms:.4f} ms/step")
         del qa, ka, va
 
+    # the same step captured once in a HIP graph and replayed: the kernels
+    # without the host's per-call launch work (every call takes preallocated
+    # outputs and workspace, so the capture allocates nothing)
+    graph_rec = None
+    if args.graph_steps > 0:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for kn in kernels:
+                launch(kn)
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.graph_steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize(dev)
+        g_ms = g0.elapsed_time(g1) / args.graph_steps
+        graph_rec = {"ms_per_step": round(g_ms, 5), "steps": args.graph_steps,
+                     "over_direct_calls": round(g_ms / ms_per_step, 4)}
+        log(f"[bench] HIP graph replay: {g_ms:.4f} ms/step")
+        del graph
+
     layout_rec = None
     if args.layout_steps > 0 and w.mask == "block":
         layout_rec = token_order_timing(attn, torch, w, q, k, v, do, ws, kw, fused, o, lse, dq, dk,
@@ -585,6 +610,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "parity": parity,
         "autograd": autograd_rec,
+        "hip_graph": graph_rec,
         "token_order": layout_rec,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count, "torch": torch.__version__,
