@@ -20,6 +20,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              workload on this host, in the same unit
   parity     GPU outputs of the sampled slices against the oracle, checked
              outside the timed region
+  timing     p10 / median / p90 of the step and of each kernel over the timed
+             steps ("warm": back to back) and over steps each preceded by a
+             1 GiB read that evicts every cache ("cache_flushed"), with the
+             dominant kernel's roofline fraction at each median
 
 Workloads (``--workload``): block_local_hiera (default; Hiera-Base mask-unit
 attention, 49 windows of 64 tokens, B=128, d=96), block_pooled_hiera (the
@@ -161,6 +165,20 @@ def stored_traffic(workload: str, kernel: str):
         return None
     val = fields.get(f"traffic_bytes_per_launch.{kernel}")
     return float(val) if val is not None else None
+
+
+def step_spread(events, kernels) -> dict:
+    """p10 / median / p90 of the step time and of each kernel's time over
+    the steps, from HIP events recorded before the step and after each
+    kernel of it."""
+    def pct(xs):
+        a = np.asarray(xs, dtype=np.float64)
+        return {"p10": round(float(np.percentile(a, 10)), 5),
+                "median": round(float(np.median(a)), 5),
+                "p90": round(float(np.percentile(a, 90)), 5)}
+    return {"ms_per_step": pct([e[0].elapsed_time(e[-1]) for e in events]),
+            "per_kernel_ms": {kn: pct([e[i].elapsed_time(e[i + 1]) for e in events])
+                              for i, kn in enumerate(kernels)}}
 
 
 # ------------------------------------------------------- interleaved heads
@@ -361,6 +379,12 @@ def main() -> int:
                          "with every tensor in Hiera's token order (strided entry points), "
                          "and the same step done by copying to and from the contiguous "
                          "layout (0 skips it)")
+    ap.add_argument("--cold-steps", type=int, default=50,
+                    help="after the timed region, time this many steps each preceded by "
+                         "a read of --flush-mib MiB that evicts the inputs from the L2 "
+                         "and the Infinity Cache (0 skips it)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="size of the cache-evicting read before each cold step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run a plain device copy of this "
                          "many MiB 5 times (a known-size reference for HBM counters)")
@@ -454,6 +478,7 @@ def main() -> int:
     ms_per_step = total_ms / K
     kern_ms = {kn: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
                for i, kn in enumerate(kernels)}
+    warm_spread = step_spread(ev, kernels)
     log(f"[bench] {ms_per_step:.4f} ms/step; per kernel (ms): "
         + ", ".join(f"{kn} {kern_ms[kn]:.4f}" for kn in kernels))
 
@@ -513,6 +538,31 @@ def main() -> int:
         log(f"[bench] HIP graph replay: {g_ms:.4f} ms/step")
         del graph
 
+    # cache-flushed steps: before each, a read of a buffer four times the
+    # 256 MB Infinity Cache evicts Q, K, V, dO (and the previous step's
+    # outputs) from every cache, so the forward reads them from HBM.  A read,
+    # not a write: a write would leave the caches full of dirty lines whose
+    # write-back the next kernel would pay for (measured: the block-local
+    # forward 0.049 -> 0.102 ms after a 1 GiB fill)
+    cold_rec = None
+    if args.cold_steps > 0:
+        flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+               for _ in range(args.cold_steps)]
+        torch.cuda.synchronize(dev)
+        for s in range(args.cold_steps):
+            torch.sum(flush, dim=0, out=sink)
+            cev[s][0].record()
+            for i, kn in enumerate(kernels):
+                launch(kn)
+                cev[s][i + 1].record()
+        torch.cuda.synchronize(dev)
+        cold_rec = step_spread(cev, kernels)
+        cold_rec.update(steps=args.cold_steps, flush_mib=args.flush_mib)
+        log(f"[bench] cache-flushed steps: median {cold_rec['ms_per_step']['median']:.4f} ms/step")
+        del flush, sink
+
     layout_rec = None
     if args.layout_steps > 0 and w.mask == "block":
         layout_rec = token_order_timing(attn, torch, w, q, k, v, do, ws, kw, fused, o, lse, dq, dk,
@@ -558,6 +608,14 @@ def main() -> int:
     roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = {"flops": wk["flops"], "bytes": wk["bytes"]}
+    timing = {"warm": warm_spread, "cache_flushed": cold_rec}
+    for rec_t in timing.values():
+        if rec_t is not None:
+            # the dominant kernel's median duration against its roofline
+            t_med = rec_t["per_kernel_ms"][dom]["median"] * 1e-3
+            rec_t["roofline_frac_at_median"] = round(
+                (wk["flops"] / t_med / 1e12 / peak_c) if mfma_bound
+                else (wk["bytes"] / t_med / 1e9 / HBM_PEAK_GBS), 4)
 
     # ---- outputs for the parity check (a full fwd + bwd through attn_bwd)
     o2, lse2 = attn.fwd(q, k, v, **kw)
@@ -610,6 +668,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "parity": parity,
         "autograd": autograd_rec,
+        "timing": timing,
         "hip_graph": graph_rec,
         "token_order": layout_rec,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),

@@ -248,12 +248,17 @@ def fwd(q, k, v, mask: str = "none", window: int = 0, scale=None, out=None, lse=
     return o, lse
 
 
-def bwd_fused(q, k, v, mask: str = "none", window: int = 0) -> bool:
-    """True when ``bwd`` runs as one fused kernel for these tensors (then
-    ``passes`` must be PASS_ALL)."""
+def bwd_fused(q, k, v, mask: str = "none", window: int = 0) -> int:
+    """Nonzero when ``bwd`` runs as one fused kernel for these tensors:
+    FUSED_LOCAL (block-local windows; ``passes`` must then be PASS_ALL) or
+    FUSED_SHORT (every key of a (b, h) in one workgroup; a partial ``passes``
+    set runs the general passes); 0 otherwise."""
     B, H, Nq, Nk, d, mask, window = _geometry(q, k, v, *_mask_args(q, mask, window))
-    return load_library().attn_bwd_fused(DTYPE_CODES[q.dtype], B, H, Nq, Nk, d,
-                                         MASK_CODES[mask], window) == 1
+    return int(load_library().attn_bwd_fused(DTYPE_CODES[q.dtype], B, H, Nq, Nk, d,
+                                             MASK_CODES[mask], window))
+
+
+FUSED_LOCAL, FUSED_SHORT = 1, 2
 
 
 def workspace_bytes(B: int, H: int, Nq: int) -> int:

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 OUT = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_bf16.hip", "attn_bf16_local.hip", "attn_fp32.hip", "premix.hip"]
+SOURCES = ["attn_api.cpp", "attn_bf16.hip", "attn_bf16_local.hip", "attn_bf16_short.hip", "attn_fp32.hip",
+           "premix.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -449,7 +449,9 @@ int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int6
                    int64_t window) {
   if (check_geometry(dtype, B, H, Nq, Nk, d, 1.0f, mask, window) != ATTN_OK) return 0;
   if (!is16(dtype)) return 0;
-  return make_geom(mask, Nq, Nk, window).local64() ? 1 : 0;
+  const attn::MaskGeom g = make_geom(mask, Nq, Nk, window);
+  if (g.local64()) return 1;
+  return attn::short_keys(g, (int)d) ? 2 : 0;
 }
 
 int attn_fwd_strided(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,

@@ -992,6 +992,9 @@ int launch_bwd_16(const BwdArgs& a, bool f16, int d, hipStream_t s, int passes) 
     if (passes != kPassAll) return (int)hipErrorInvalidValue;
     return launch_bwd_16_local(a, f16, d, s);
   }
+  // every key of a (b, h) in one workgroup: the whole backward is one fused
+  // kernel; a partial pass set runs the general passes
+  if (passes == kPassAll && short_keys(a.mg, d)) return launch_bwd_16_short(a, f16, d, s);
   return f16 ? launch_bwd_e<F16>(a, d, s, passes) : launch_bwd_e<Bf16>(a, d, s, passes);
 }
 

@@ -126,6 +126,16 @@ struct MaskGeom {
   }
 };
 
+// The fused backward for short key sequences holds every key of a (b, h) in
+// one workgroup: one wave per 32 keys and a dQ wave, 8 waves at most.  It
+// loops over the query rows in slabs of 32, so long query sequences are left
+// to the general passes.
+constexpr int kShortKeys = 224;
+constexpr int kShortRows = 1024;
+inline bool short_keys(const MaskGeom& g, int d) {
+  return !g.local64() && (d == 64 || d == 96) && g.nk <= kShortKeys && g.nq <= kShortRows;
+}
+
 // elements of one dS block: 2 key chunks x 64 lanes x 8 bf16
 constexpr int kDsBlockElems = 1024;
 
@@ -271,6 +281,8 @@ int launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t s);
 // single-tile 16-bit kernels for MaskGeom::local64() (forward; fused backward)
 int launch_fwd_16_local(const FwdArgs& a, bool f16, int d, hipStream_t s);
 int launch_bwd_16_local(const BwdArgs& a, bool f16, int d, hipStream_t s);
+// fused 16-bit backward for short_keys() (one workgroup per (b, h))
+int launch_bwd_16_short(const BwdArgs& a, bool f16, int d, hipStream_t s);
 int launch_bwd_fp32(const BwdArgs& a, int d, hipStream_t s, int passes);
 // IHA premix (16-bit types)
 int launch_premix_fwd(const PremixArgs& a, bool f16, int d, hipStream_t s);

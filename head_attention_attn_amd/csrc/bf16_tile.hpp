@@ -96,7 +96,8 @@ __device__ __forceinline__ typename E::v8 lds_tr8(const uint16_t* tile, int r0, 
 // base + 16 * lane, with no register staging: lane slot p is LDS chunk
 // position p, so the lane fetches the logical chunk that the layout stores
 // there; lanes on padding slots are switched off.  Rows >= n are filled from
-// row n - 1 (finite values that every kernel masks out).  The loads count on
+// row n - 1 (finite values that every kernel masks out); the first row r0
+// must be below n (contiguous rows address from row r0).  The loads count on
 // vmcnt; the caller waits for them (__syncthreads() does) before reading.
 template <int ROWS, int D, int NT, bool SR>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, const RowMap& rm,

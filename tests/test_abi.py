@@ -95,12 +95,15 @@ def test_workspace_size_ds_counts_visible_blocks(lib, nq, nk, mask, window):
 
 def test_pooled_block_single_tile_dispatch(lib):
     """Key windows dividing 64 whose query windows divide them run as single
-    tiles (fused backward), pooled or not; other block shapes do not."""
+    tiles (fused backward, 1), pooled or not; other block shapes with at
+    most 224 keys take the short-sequence fused backward (2), longer ones
+    the general passes (0)."""
     assert lib.attn_bwd_fused(0, 1, 1, 3136, 3136, 96, 3, 64) == 1
     assert lib.attn_bwd_fused(0, 1, 1, 784, 3136, 96, 3, 64) == 1     # 16 query rows per window
     assert lib.attn_bwd_fused(0, 1, 1, 4, 64, 96, 3, 16) == 1         # one query row per window
-    assert lib.attn_bwd_fused(0, 1, 1, 12, 64, 96, 3, 16) == 0        # 3 rows per window of 16
-    assert lib.attn_bwd_fused(0, 1, 1, 20, 80, 96, 3, 80) == 0        # window 80 does not divide 64
+    assert lib.attn_bwd_fused(0, 1, 1, 12, 64, 96, 3, 16) == 2        # 3 rows per window of 16
+    assert lib.attn_bwd_fused(0, 1, 1, 20, 80, 96, 3, 80) == 2        # window 80 does not divide 64
+    assert lib.attn_bwd_fused(0, 1, 1, 60, 240, 96, 3, 80) == 0       # ... 240 keys
     assert lib.attn_bwd_fused(1, 1, 1, 784, 3136, 96, 3, 64) == 0     # fp32
     assert lib.attn_bwd_fused(2, 1, 1, 784, 3136, 96, 3, 64) == 1     # fp16
     assert lib.attn_bwd_fused(0, 1, 1, 15, 64, 96, 3, 16) == 0        # invalid: 4 windows, 15 rows
@@ -209,13 +212,25 @@ def test_bwd_validation(lib, kw, status):
 
 
 def test_fused_backward_predicate(lib):
-    """The backward is one fused kernel exactly for bf16 block-local attention
-    whose window divides 64; invalid geometry reports 0."""
-    f = lambda dtype, n, mask, w, d=96: lib.attn_bwd_fused(dtype, 2, 1, n, n, d, mask, w)
+    """The backward is one fused kernel for 16-bit block-local attention whose
+    window divides 64 (1) and for 16-bit attention with at most 224 keys and
+    1024 query rows at d = 64 or 96 (2); invalid geometry reports 0."""
+    f = lambda dtype, n, mask, w, d=96, nq=None: lib.attn_bwd_fused(
+        dtype, 2, 1, n if nq is None else nq, n, d, mask, w)
     for w in (1, 2, 4, 8, 16, 32, 64):
         assert f(BF16, 3136, 3, w) == 1
+        assert f(FP16, 3136, 3, w) == 1
     assert f(BF16, 3136, 3, 7 * 64) == 0        # window 448 > 64
-    assert f(BF16, 192, 3, 48) == 0             # 48 does not divide 64
+    assert f(BF16, 192, 3, 48) == 2             # 48 does not divide 64; 192 keys
+    assert f(BF16, 960, 3, 48) == 0             # ... 960 keys
+    for mask, w in ((0, 0), (1, 0), (2, 37)):
+        assert f(BF16, 196, mask, w) == 2       # short sequences, any mask
+        assert f(FP16, 224, mask, w, d=64) == 2
+        assert f(BF16, 225, mask, w) == 0       # 225 keys
+        assert f(BF16, 196, mask, w, d=128) == 0
+        assert f(FP32, 196, mask, w) == 0
+    assert f(BF16, 100, 0, 0, nq=1024) == 2
+    assert f(BF16, 100, 0, 0, nq=1025) == 0     # long query sequence
     assert f(FP32, 3136, 3, 64) == 0            # fp32 path is not fused
     assert f(BF16, 3136, 0, 64) == 0            # mask none
     assert f(BF16, 3136, 2, 64) == 0            # sliding

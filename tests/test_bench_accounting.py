@@ -92,3 +92,21 @@ def test_iha_workload_accounting():
     assert work["premix"]["bytes"] == 3 * 2 * (x + 4 * x + 20 * 4 * 20)
     assert work["premix"]["flops"] == 3 * 2 * 20 * (4 * x)
     assert "premix" not in bench.kernel_work(WORKLOADS["causal_lm"], 1)
+
+
+def test_step_spread_percentiles():
+    """p10 / median / p90 of the step and per-kernel times from events
+    recorded before a step and after each of its kernels."""
+    class Ev:
+        def __init__(self, t):
+            self.t = t
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    # step s: fwd takes 1 + s ms, bwd 2 ms; steps 0..10
+    events = [[Ev(100.0 * s), Ev(100.0 * s + 1 + s), Ev(100.0 * s + 3 + s)] for s in range(11)]
+    rec = bench.step_spread(events, ("fwd", "bwd"))
+    assert rec["per_kernel_ms"]["fwd"] == {"p10": 2.0, "median": 6.0, "p90": 10.0}
+    assert rec["per_kernel_ms"]["bwd"] == {"p10": 2.0, "median": 2.0, "p90": 2.0}
+    assert rec["ms_per_step"] == {"p10": 4.0, "median": 8.0, "p90": 12.0}

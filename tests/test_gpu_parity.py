@@ -301,10 +301,13 @@ def test_block_pooled_queries(d, nw, w, wq, single_tile):
     """Block mask with pooled queries: Nk / w windows of w keys each hold
     Nq / (Nk / w) = wq query rows (Hiera's q_stride = w / wq).  Key windows
     dividing 64 with wq dividing w run as single tiles (64 keys and their
-    64 wq / w query rows), the rest on the general kernels."""
+    64 wq / w query rows), the rest on the fused short-sequence kernel (at
+    most 224 keys, d <= 96) or the general kernels."""
     nq, nk = nw * wq, nw * w
     q, k, v, _ = make_inputs(1, 1, nq, nk, d, "bf16", seed=14)
-    assert attn.binding.bwd_fused(q.cuda(), k.cuda(), v.cuda(), mask="block", window=w) == single_tile
+    kind = (attn.binding.FUSED_LOCAL if single_tile else
+            attn.binding.FUSED_SHORT if nk <= 224 and d <= 96 else 0)
+    assert attn.binding.bwd_fused(q.cuda(), k.cuda(), v.cuda(), mask="block", window=w) == kind
     parity_case(2, 2, nq, nk, d, "bf16", "block", w, seed=14)
 
 
