@@ -186,17 +186,25 @@ enum attn_pass {
 };
 
 /*
- * attn_bwd_fused -- 1 when attn_bwd runs as ONE fused kernel for these
- * arguments, else 0 (also 0 for arguments attn_bwd would reject).  Fused:
- * bf16 or fp16 block-local attention whose window divides 64 and whose query rows per
- * window Wq = Nq / (Nk / window) divide the window (Wq = window, or pooled
- * queries with an integer q_stride = window / Wq), where every query row
- * sees keys of its own 64-key tile only ("hiera-optim 0.1.0" sdist,
- * mask_unit.py: mask-unit windows as independent dense attentions).  One
- * workgroup then holds a whole tile: its dK/dV waves and its dQ waves run the
- * two backward passes side by side, the row sums D_i are formed in-tile as
- * sum_j P_ij dP_ij, the workspace is not used and O is not read.  In the
- * fused case attn_bwd_passes accepts only ATTN_PASS_ALL.
+ * attn_bwd_fused -- nonzero when attn_bwd runs as ONE fused kernel for these
+ * arguments, else 0 (also 0 for arguments attn_bwd would reject).
+ *   1  bf16 or fp16 block-local attention whose window divides 64 and whose
+ *      query rows per window Wq = Nq / (Nk / window) divide the window (Wq =
+ *      window, or pooled queries with an integer q_stride = window / Wq),
+ *      where every query row sees keys of its own 64-key tile only
+ *      ("hiera-optim 0.1.0" sdist, mask_unit.py: mask-unit windows as
+ *      independent dense attentions).  One workgroup holds a whole tile: its
+ *      dK/dV waves and its dQ waves run the two backward passes side by
+ *      side.  attn_bwd_passes then accepts only ATTN_PASS_ALL.
+ *   2  otherwise, bf16 or fp16 with d = 64 or 96, Nk <= 224 and Nq <= 1024,
+ *      any mask (the global-attention stages of Hiera at 224^2 have 196 and
+ *      49 tokens: "Hiera: A Hierarchical Vision Transformer without the
+ *      Bells-and-Whistles", Sec. 3): one workgroup holds every key of a
+ *      (b, h) and loops over its query rows.  attn_bwd_passes with
+ *      ATTN_PASS_ALL runs the fused kernel; a partial pass set runs the
+ *      general passes.
+ * In both cases the row sums D_i are formed in-kernel as sum_j P_ij dP_ij,
+ * the workspace is not used and O is not read.
  */
 ATTN_API int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                             int mask, int64_t window);
