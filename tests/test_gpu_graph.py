@@ -26,6 +26,7 @@ def _step(q, k, v, do, mask, window, keep_ds):
     (1, 3, 1000, 128, "causal", 0, True),      # general kernels, dS kept for the dQ pass
     (2, 2, 700, 64, "sliding", 100, False),    # general kernels, dQ recomputed
     (8, 1, 3136, 96, "block", 64, True),       # fused single-tile backward
+    (16, 4, 196, 96, "none", 0, True),         # fused short-sequence backward
 ])
 def test_graph_replays_match_eager(B, H, N, d, mask, window, keep_ds):
     say(f"[graph] {mask} B={B} H={H} N={N} d={d}")
