@@ -213,7 +213,10 @@ ATTN_API int attn_bwd_fused(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t
  * attn_bwd_passes -- attn_bwd restricted to the passes in the bit set
  * `passes` (1..ATTN_PASS_ALL; anything else is ATTN_ERR_INVALID_ARG),
  * enqueued in the order row sums, dK/dV, dQ.  Where attn_bwd_fused() is 1,
- * any set but ATTN_PASS_ALL is ATTN_ERR_UNSUPPORTED.  attn_bwd is
+ * any set but ATTN_PASS_ALL is ATTN_ERR_UNSUPPORTED; where it is 2,
+ * ATTN_PASS_ALL runs the fused kernel and any other set the general passes
+ * (so a caller that enqueues the three bits one call at a time gets the
+ * general passes).  attn_bwd is
  * attn_bwd_passes(ATTN_PASS_ALL, ...).  Every argument is validated exactly
  * as in attn_bwd, including the outputs a pass does not write.  The dK/dV
  * and dQ passes read D from the workspace, so they need a row-sum pass with
