@@ -181,6 +181,28 @@ def step_spread(events, kernels) -> dict:
                               for i, kn in enumerate(kernels)}}
 
 
+def stored_clock(workload: str, kernel: str):
+    """The clock (GHz) the kernel ran at in the rocprofv3 counter run of
+    profiles/mfma_<workload>.txt (GRBM_GUI_ACTIVE cycles over the dispatch
+    duration), when that run was taken from the current kernel sources and
+    the kernel was long enough to time it; else None."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    digest, clock = None, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("source_sha256:"):
+                digest = line.split(":", 1)[1].strip()
+            parts = line.split()
+            if len(parts) >= 3 and parts[0] == kernel:
+                try:
+                    clock = float(parts[2])
+                except ValueError:
+                    clock = None
+    return clock if digest == source_digest() else None
+
+
 # ------------------------------------------------------- interleaved heads
 
 def iha_setup(attn, torch, w, dev):
@@ -608,6 +630,12 @@ def main() -> int:
     roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = {"flops": wk["flops"], "bytes": wk["bytes"]}
+    # the peak at the clock the dominant kernel ran at under load (the MFMA
+    # peak is quoted at 2.4 GHz; MFMA-heavy kernels run at 1.8-2.1 GHz)
+    clk = stored_clock(w.name, dom)
+    clock_rec = None if clk is None else {
+        "kernel": dom, "ghz": clk, "source": f"profiles/mfma_{w.name}.txt",
+        "pct_of_bf16_mfma_peak_at_clock": round(100 * value / (MFMA_BF16_PEAK_TFLOPS * clk / 2.4), 3)}
     timing = {"warm": warm_spread, "cache_flushed": cold_rec}
     for rec_t in timing.values():
         if rec_t is not None:
@@ -663,6 +691,7 @@ def main() -> int:
         "data": "synthetic i.i.d. N(0,1) Q, K, V, dO (seed 0), resident in HBM",
         "config": cfg,
         "pct_of_bf16_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 3),
+        "measured_clock": clock_rec,
         "per_kernel_ms": {kn: round(kern_ms[kn], 5) for kn in kernels},
         "roofline": roof,
         "cpu_baseline": cpu,
