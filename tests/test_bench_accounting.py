@@ -110,3 +110,26 @@ def test_step_spread_percentiles():
     assert rec["per_kernel_ms"]["fwd"] == {"p10": 2.0, "median": 6.0, "p90": 10.0}
     assert rec["per_kernel_ms"]["bwd"] == {"p10": 2.0, "median": 2.0, "p90": 2.0}
     assert rec["ms_per_step"] == {"p10": 4.0, "median": 8.0, "p90": 12.0}
+
+
+def test_stored_profiles_follow_the_sources(tmp_path, monkeypatch):
+    """Counter readings stored under profiles/ are used only while their
+    recorded source digest matches the kernel sources; otherwise the bench
+    reports null."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    digest = bench.source_digest()
+    (prof / "traffic_w.txt").write_text(
+        f"# header\nsource_sha256: {digest}\ntraffic_bytes_per_launch.bwd: 123.0\n")
+    (prof / "mfma_w.txt").write_text(
+        f"# header\nsource_sha256: {digest}\nkernel dur_us clock_GHz\nbwd 64.5 2.48\nfwd 25.0 -\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda: digest)
+    assert bench.stored_traffic("w", "bwd") == 123.0
+    assert bench.stored_clock("w", "bwd") == 2.48
+    assert bench.stored_clock("w", "fwd") is None          # too short to time
+    assert bench.stored_traffic("w", "fwd") is None
+    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 64)
+    assert bench.stored_traffic("w", "bwd") is None
+    assert bench.stored_clock("w", "bwd") is None
+    assert bench.stored_clock("missing", "bwd") is None
