@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int rlo = qvalid ? mg.row_lo(myq) : 0;
   const int rhi = qvalid ? mg.row_hi(myq) : 0;
   const float sl2 = a.scale * kLog2e;
-  const int t0 = (lo / BN) * BN;
+  const int t0 = range_tile_row(lo, BN, 0);
 
   if (lo < hi) {
     dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   mg.query_range(k0, k1, &lo, &hi);
   if (wk0 < a.nk) mg.query_range(wk0, wk1, &wlo, &whi);
   const float sl2 = a.scale * kLog2e;
-  const int t0 = (lo / BQ) * BQ;
+  const int t0 = range_tile_row(lo, BQ, 0);
 
   auto load = [&](uint16_t* q_l, uint16_t* g_l, float* s_l, int r0) {
     dma_tile<BQ, D, NT, SR>(q_l, Q, a.rq, r0, a.nq, tid);
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   int lo, hi, wlo = 0, whi = 0;
   mg.query_range(k0, k1, &lo, &hi);
   if (wk0 < a.nk) mg.query_range(wk0, wk1, &wlo, &whi);
-  const int t0 = (lo / BQ) * BQ;
+  const int t0 = range_tile_row(lo, BQ, 0);
   const int ntiles = lo < hi ? (hi - t0 + BQ - 1) / BQ : 0;
 
   // Q / dO / lse / D of tile j are fetched into registers one step before
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int jq = wa / 32;  // this wave's query block
   int lo, hi;
   mg.key_range(i0, i1, &lo, &hi);
-  const int t0 = (lo / BN) * BN;
+  const int t0 = range_tile_row(lo, BN, 0);
 
   // running block cursor: index of key block `kbn`'s first dS block
   int kbn = t0 / 32;
@@ -818,7 +818,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int rlo = qvalid ? mg.row_lo(myq) : 0;
   const int rhi = qvalid ? mg.row_hi(myq) : 0;
   const float sl2 = a.scale * kLog2e;
-  const int t0 = (lo / BN) * BN;
+  const int t0 = range_tile_row(lo, BN, 0);
 
   if (lo < hi) {
     dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);

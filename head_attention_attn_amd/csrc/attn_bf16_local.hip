@@ -42,29 +42,12 @@ namespace {
 
 constexpr int kTile = 64;  // keys per tile
 
-// Tile geometry: key window w = 1 << lw, query rows per window wq = 1 << lq;
-// tile t holds keys [64 t, 64 t + 64) and query rows [QT t, QT t + QT) with
-// QT = (64 >> lw) << lq.  Query row r and key c of a tile (both counted from
-// the tile's start, which is window-aligned on both sides) see each other iff
-// row r is real and r >> lq == c >> lw.  A real row's window keys all exist
-// (Nk is a multiple of w), so keys past Nk are never visible.
-struct LocalTile {
-  int lw, lq, qt;  // log2 w, log2 wq, query rows per tile
-  int tq0, qend;   // first query row of the tile, end of its real rows
-  __device__ __forceinline__ bool real(int r) const { return tq0 + r < qend; }  // implies r < qt
-  // bitwise, not short-circuit: evaluated per score element without branches
-  __device__ __forceinline__ bool vis(int r, int c) const { return real(r) & ((r >> lq) == (c >> lw)); }
-};
-
-__device__ __forceinline__ LocalTile local_tile(int tile, int nq, int lw, int lq) {
-  LocalTile t;
-  t.lw = lw;
-  t.lq = lq;
-  t.qt = (kTile >> lw) << lq;
-  t.tq0 = tile * t.qt;
-  t.qend = min(nq, t.tq0 + t.qt);
-  return t;
-}
+// Tile geometry (LocalTile, attn_common.hpp): tile t holds keys
+// [64 t, 64 t + 64) and query rows [QT t, QT t + QT).  Query row r and key c
+// of a tile (both counted from the tile's start, which is window-aligned on
+// both sides) see each other iff row r is real and r >> lq == c >> lw.  A
+// real row's window keys all exist (Nk is a multiple of w), so keys past Nk
+// are never visible.
 
 // ------------------------------------------------------------------ forward
 
@@ -84,8 +67,8 @@ __global__ __launch_bounds__(2 * QR) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int wave = wave_id(tid);
   const int bh = blockIdx.x / ntile;
   const int tile = blockIdx.x % ntile;
-  const int tk0 = tile * kTile;
   const LocalTile lt = local_tile(tile, a.nq, lw, lq);
+  const int tk0 = lt.tk0;
 
   const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
   const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
@@ -189,8 +172,8 @@ __global__ __launch_bounds__(128 + 2 * QR) __attribute__((amdgpu_waves_per_eu(3)
   const int wave = wave_id(tid);
   const int bh = blockIdx.x / ntile;
   const int tile = blockIdx.x % ntile;
-  const int tk0 = tile * kTile;
   const LocalTile lt = local_tile(tile, a.nq, lw, lq);
+  const int tk0 = lt.tk0;
   const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
   const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
   const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kNT) void bwd_short_kernel(BwdArgs a) {
   const int wave = wave_id(tid);
   const int bh = blockIdx.x;
   const int nq = a.nq, nk = a.nk;
-  const int nkb = (nk + 31) / 32;  // key blocks, <= kKeyWaves
+  const int nkb = short_key_blocks(nk);  // key blocks, <= kKeyWaves
   const MaskGeom mg = a.mg;
   const bool dq_wave = wave == kKeyWaves;
 
@@ -104,11 +104,11 @@ __global__ __launch_bounds__(kNT) void bwd_short_kernel(BwdArgs a) {
   // every key block's K and V rows (32-row tiles laid end to end are one tall
   // tile: the layout's swizzle repeats every 16 rows).  The dQ products run
   // over all kKeyWaves blocks, unrolled: blocks past the keys hold a copy of
-  // the last key block (finite values; a tile load must start at a row < nk)
-  // and their dS stays zero, as do their partial row sums.
+  // the last key block (short_k_block_row; a tile load must start at a row
+  // < nk) and their dS stays zero, as do their partial row sums.
 #pragma unroll
   for (int b = 0; b < kKeyWaves; ++b)
-    dma_tile<32, D, kNT, SR>(sK + b * SE, K, a.rk, 32 * min(b, nkb - 1), nk, tid);
+    dma_tile<32, D, kNT, SR>(sK + b * SE, K, a.rk, short_k_block_row(b, nk), nk, tid);
   for (int b = 0; b < nkb; ++b) dma_tile<32, D, kNT, SR>(sV + b * SE, V, a.rv, 32 * b, nk, tid);
   for (int i = tid; i < kKeyWaves * 1024 / 8; i += kNT) reinterpret_cast<uint4*>(sDS)[i] = uint4{0, 0, 0, 0};
   for (int i = tid; i < kKeyWaves * 32; i += kNT) sDp[i] = 0.f;

@@ -139,6 +139,57 @@ inline bool short_keys(const MaskGeom& g, int d) {
 // elements of one dS block: 2 key chunks x 64 lanes x 8 bf16
 constexpr int kDsBlockElems = 1024;
 
+// ---------------------------------------------------------------- tile loads
+
+// Every kernel moves rows a tile at a time.  The direct global -> LDS tile
+// load addresses a tile of contiguous rows from its first row r0, so r0 must
+// lie inside the tensor's n rows (rows past n inside the tile read row n - 1).
+// The first rows of all tile loads come from the functions below, which
+// tests/host/tile_range_check.cpp enumerates on the host for every geometry
+// the kernels accept, checking r0 < n.
+
+// A loop over the visible range [lo, hi) (lo < hi <= n) in T-row tiles aligned
+// to multiples of T: tile t starts at range_tile_row(lo, T, t) and is loaded
+// only while that row is below hi.
+ATTN_HD int range_tile_row(int lo, int T, int t) { return (lo / T) * T + t * T; }
+
+// The short-sequence backward's key blocks of 32 rows: nk keys fill
+// short_key_blocks(nk) blocks.  Its unrolled loops run over all
+// kShortKeys / 32 blocks; block b's K rows are loaded from row
+// short_k_block_row(b, nk), which repeats the last real block for the blocks
+// past the keys (finite values whose dS and partial row sums stay zero).
+// Loading block b from row 32 b would address rows past the slice for the
+// blocks past the keys, i.e. whenever nk <= kShortKeys - 32.
+ATTN_HD int short_key_blocks(int nk) { return (nk + 31) / 32; }
+ATTN_HD int short_k_block_row(int b, int nk) {
+  const int last = short_key_blocks(nk) - 1;
+  return 32 * (b < last ? b : last);
+}
+
+// Single-tile block-local geometry (MaskGeom::local64): key window w = 1 << lw,
+// query rows per window wq = 1 << lq; tile t holds keys [64 t, 64 t + 64) and
+// query rows [QT t, QT t + QT) with QT = (64 >> lw) << lq, of which the rows
+// below qend are real.  For t < ceil(nk / 64) both first rows are inside
+// their tensors: 64 t < nk, and QT t < nq since nq = (nk >> lw) << lq.
+struct LocalTile {
+  int lw, lq, qt;  // log2 w, log2 wq, query rows per tile
+  int tk0;         // first key of the tile
+  int tq0, qend;   // first query row of the tile, end of its real rows
+  ATTN_HD bool real(int r) const { return tq0 + r < qend; }  // implies r < qt
+  // bitwise, not short-circuit: evaluated per score element without branches
+  ATTN_HD bool vis(int r, int c) const { return real(r) & ((r >> lq) == (c >> lw)); }
+};
+ATTN_HD LocalTile local_tile(int tile, int nq, int lw, int lq) {
+  LocalTile t;
+  t.lw = lw;
+  t.lq = lq;
+  t.qt = (64 >> lw) << lq;
+  t.tk0 = tile * 64;
+  t.tq0 = tile * t.qt;
+  t.qend = t.tq0 + t.qt < nq ? t.tq0 + t.qt : nq;
+  return t;
+}
+
 // ---------------------------------------------------------------- row maps
 
 // Where the rows of one [B][H][N][d] tensor live.  Row j (token j) of slice

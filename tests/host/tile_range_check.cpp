@@ -137,6 +137,79 @@ static void check_tile_order(int BH, int nt) {
     }
 }
 
+// First rows of every tile load (attn_common.hpp, "tile loads"): the direct
+// global -> LDS load addresses a tile from its first row, which must be one
+// of the tensor's rows.
+static int imin_(int a, int b) { return a < b ? a : b; }
+
+// General kernels: a workgroup owns rows [a, a + BM) of one tensor (query rows
+// when by_query, else keys) and walks the visible range of the other in T-row
+// tiles from range_tile_row(lo, T, 0) while the tile's first row is below hi.
+static void check_range_loads(const MaskGeom& g, bool by_query, int BM, int T, const char* kernel) {
+  const int n_own = by_query ? g.nq : g.nk;
+  const int n_load = by_query ? g.nk : g.nq;
+  for (int a = 0; a < n_own; a += BM) {
+    const int b = imin_(a + BM, n_own);
+    int lo, hi;
+    if (by_query)
+      g.key_range(a, b, &lo, &hi);
+    else
+      g.query_range(a, b, &lo, &hi);
+    if (lo >= hi) continue;
+    CHECK(lo >= 0 && hi <= n_load, "%s range [%d,%d) outside %d rows (m%d W%d %dx%d)\n", kernel, lo, hi, n_load,
+          g.mode, g.window, g.nq, g.nk);
+    for (int t = 0;; ++t) {
+      const int r0 = attn::range_tile_row(lo, T, t);
+      if (r0 >= hi) break;
+      CHECK(r0 >= 0 && r0 < n_load, "%s tile row %d of %d rows (m%d W%d %dx%d, wg rows %d)\n", kernel, r0, n_load,
+            g.mode, g.window, g.nq, g.nk, a);
+    }
+  }
+}
+
+static void check_general_loads(const MaskGeom& g) {
+  check_range_loads(g, true, 128, 64, "fwd");          // 128 query rows, 64-key K/V tiles
+  check_range_loads(g, false, 128, 64, "dkdv d<=96");  // 128 keys, 64-row Q/dO tiles
+  check_range_loads(g, false, 128, 32, "dkdv d=128");  // 128 keys, 32-row Q/dO tiles
+  check_range_loads(g, true, 128, 128, "dq kept dS");  // 128 query rows, 128-key K tiles
+  check_range_loads(g, true, 128, 64, "dq");           // 128 query rows, 64-key K/V tiles
+}
+
+// The short-sequence backward, for every (Nq, Nk) and mask it accepts: key
+// blocks (K from short_k_block_row, V from 32 b for the real blocks) and
+// 32-row query slabs.
+static long short_geometries = 0;
+static void check_short_loads(const MaskGeom& g) {
+  for (int d : {64, 96}) {
+    if (!attn::short_keys(g, d)) continue;
+    ++short_geometries;
+    const int nkb = attn::short_key_blocks(g.nk);
+    CHECK(nkb >= 1 && nkb <= attn::kShortKeys / 32, "short: %d key blocks for nk %d\n", nkb, g.nk);
+    for (int b = 0; b < attn::kShortKeys / 32; ++b) {
+      const int r0 = attn::short_k_block_row(b, g.nk);
+      CHECK(r0 >= 0 && r0 < g.nk, "short: K block %d at row %d of %d (nq %d m%d d%d)\n", b, r0, g.nk, g.nq,
+            g.mode, d);
+      if (b < nkb) CHECK(32 * b < g.nk, "short: V block %d of %d keys\n", b, g.nk);
+    }
+    for (int s = 0; 32 * s < g.nq; ++s) CHECK(32 * s < g.nq, "short: slab %d of %d rows\n", s, g.nq);
+  }
+}
+
+// Single-tile block-local kernels: tile t < ceil(nk / 64) of every local64()
+// geometry starts inside both tensors and has at least one real query row.
+static void check_local_loads(const MaskGeom& g) {
+  if (!g.local64()) return;
+  int lw = 0, lq = 0;
+  while ((1 << lw) < g.window) ++lw;
+  while ((1 << lq) < g.window_q) ++lq;
+  for (int t = 0; 64 * t < g.nk; ++t) {
+    const attn::LocalTile lt = attn::local_tile(t, g.nq, lw, lq);
+    CHECK(lt.tk0 < g.nk && lt.tq0 < g.nq && lt.qend > lt.tq0 && lt.qend - lt.tq0 <= lt.qt,
+          "local tile %d: keys from %d of %d, rows [%d,%d) of %d (W%d Wq%d)\n", t, lt.tk0, g.nk, lt.tq0, lt.qend,
+          g.nq, g.window, g.window_q);
+  }
+}
+
 int main() {
   const int bhs[] = {1, 3, 8, 20, 80, 512};
   const int nts[] = {1, 2, 7, 32, 64};
@@ -155,6 +228,37 @@ int main() {
       for (int W = 1; W <= nk; ++W)
         if (nk % W == 0 && nq % (nk / W) == 0) check(attn::kBlock, W, nq, nk);
     }
+  // tile loads of the general kernels over a wider range of sizes
+  const int lsizes[] = {1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 256, 257, 700};
+  for (int nq : lsizes)
+    for (int nk : lsizes) {
+      check_general_loads(MaskGeom{attn::kNone, nq, nk, 0, 0});
+      check_general_loads(MaskGeom{attn::kCausal, nq, nk, 0, 0});
+      for (int W : {1, 2, 31, 64, 100, 1024}) check_general_loads(MaskGeom{attn::kSliding, nq, nk, W, 0});
+      for (int W = 1; W <= nk; ++W)
+        if (nk % W == 0 && nq % (nk / W) == 0) {
+          const MaskGeom g{attn::kBlock, nq, nk, W, nq / (nk / W)};
+          check_general_loads(g);
+          check_local_loads(g);
+        }
+    }
+  // the short-sequence backward: every Nk <= 224 and Nq <= 1024 under every mask
+  for (int nk = 1; nk <= attn::kShortKeys; ++nk)
+    for (int nq = 1; nq <= attn::kShortRows; ++nq) {
+      check_short_loads(MaskGeom{attn::kNone, nq, nk, 0, 0});
+      check_short_loads(MaskGeom{attn::kCausal, nq, nk, 0, 0});
+      for (int W : {1, 7, 64, 200, 1000}) check_short_loads(MaskGeom{attn::kSliding, nq, nk, W, 0});
+      for (int W = 1; W <= nk; ++W)
+        if (nk % W == 0 && nq % (nk / W) == 0) check_short_loads(MaskGeom{attn::kBlock, nq, nk, W, nq / (nk / W)});
+    }
+  CHECK(short_geometries > 1000000, "short: only %ld geometries checked\n", short_geometries);
+  // the check above would have caught K blocks loaded from row 32 b: that
+  // first row is past the keys for every nk <= kShortKeys - 32
+  int unclamped_bad = 0;
+  for (int nk = 1; nk <= attn::kShortKeys; ++nk)
+    for (int b = 0; b < attn::kShortKeys / 32; ++b) unclamped_bad += 32 * b >= nk;
+  CHECK(unclamped_bad > 0, "the unclamped K block rows were never out of range\n");
+  std::printf("%ld short-backward geometries\n", short_geometries);
   std::printf("%d failures\n", fails);
   return fails ? 1 : 0;
 }

@@ -64,16 +64,61 @@ def test_fused_backward_bytes():
 
 
 def test_kept_ds_bytes():
-    """With dS kept: the dK/dV pass writes 2 bytes per visible pair more, and
-    the dQ pass reads dS and K and writes dQ (no Q, dO, lse, D, V)."""
+    """With dS kept, the dK/dV pass writes 2 bytes per visible pair more and
+    the dQ pass reads them back: workspace traffic of this library, reported
+    apart; the compulsory bytes of both passes stay the method's."""
     w = WORKLOADS["causal_lm"]
     pairs = bench.visible_pairs(w.mask, w.window, w.Nq, w.Nk) * w.B * w.H
     rows = w.B * w.H * w.Nq
     plain = bench.kernel_work(w, pairs // (w.B * w.H))
     kept = bench.kernel_work(w, pairs // (w.B * w.H), kept_ds=True)
-    assert kept["dkdv"]["bytes"] == plain["dkdv"]["bytes"] + 2 * pairs
-    assert kept["dq"]["bytes"] == rows * w.d * 2 * 2 + 2 * pairs
-    assert kept["dq"]["flops"] == plain["dq"]["flops"]
+    for kn in ("dkdv", "dq"):
+        assert kept[kn]["bytes"] == plain[kn]["bytes"]
+        assert kept[kn]["flops"] == plain[kn]["flops"]
+        assert plain[kn]["workspace_bytes"] == 0
+        assert kept[kn]["workspace_bytes"] == 2 * pairs
+    # dQ step: reads Q, dO (and K, V) and the row statistics, writes dQ
+    assert plain["dq"]["bytes"] == rows * (5 * w.d * 2 + 8)
+
+
+@pytest.mark.parametrize("name,bound,mbytes,gflops", [
+    ("tiny_exact_fp32", "latency", 0.79, 0.0294),
+    ("block_local_hiera", "hbm", 928.1, 34.5),
+    ("global_vision", "hbm", 232.0, 26.4),
+    ("causal_lm", "mfma", 504.6, 1203.0),
+    ("sliding_pseudo_head", "mfma", 1009.0, 526.0),
+])
+def test_step_bound_per_config(name, bound, mbytes, gflops):
+    """The step's compulsory bytes, flops and bound class of each benchmark
+    configuration, against the figures worked out by hand from the shapes
+    (forward reads Q, K, V and writes O, lse; backward reads Q, K, V, O, dO,
+    lse and writes dQ, dK, dV; 14 d flops per visible pair; ridge point
+    2.5 PFLOP/s over 8 TB/s)."""
+    w = WORKLOADS[name]
+    sw = bench.step_work(w, bench.visible_pairs(w.mask, w.window, w.Nq, w.Nk))
+    assert sw["bound"] == bound
+    assert abs(sw["bytes"] / 1e6 - mbytes) / mbytes < 2e-3
+    assert abs(sw["flops"] / 1e9 - gflops) / gflops < 3e-3
+
+
+def test_configs_cover_the_benchmark():
+    assert bench.CONFIGS == ("tiny_exact_fp32", "block_local_hiera", "global_vision", "causal_lm",
+                             "sliding_pseudo_head")
+    assert all(c in WORKLOADS for c in bench.CONFIGS)
+
+
+def test_kernel_roofline_by_bound():
+    wk = {"flops": 2.5e12, "bytes": 8e9}
+    mf = bench.kernel_roofline(wk, "mfma", 2500.0, 2.0)   # 2.5e12 flop in 2 ms
+    assert mf["unit"] == "TFLOP/s" and mf["frac"] == 0.5
+    hb = bench.kernel_roofline(wk, "hbm", 2500.0, 2.0)    # 8 GB in 2 ms
+    assert hb["unit"] == "GB/s" and hb["frac"] == 0.5
+    assert bench.kernel_roofline(wk, "latency", 2500.0, 2.0) is None
+
+
+def test_host_cores_is_the_affinity_set():
+    import os
+    assert bench.host_cores() == len(os.sched_getaffinity(0))
 
 
 def test_iha_workload_accounting():

@@ -1,7 +1,10 @@
 """Host-side logic, on the CPU: the visibility intervals and tile predicates
 that set every kernel's loop ranges and masking, checked against a brute-force
-enumeration (tests/host/tile_range_check.cpp, built with g++ and the address
-and undefined-behaviour sanitizers)."""
+enumeration, and the first row of every tile load of every kernel, checked to
+lie inside its tensor for every geometry the kernels accept (the short-
+sequence backward: every Nk <= 224 and Nq <= 1024 under every mask)
+(tests/host/tile_range_check.cpp, built with g++ and the address and
+undefined-behaviour sanitizers)."""
 import os
 import shutil
 import subprocess
