@@ -1,8 +1,8 @@
 // attn_bf16_short.hip -- fused one-pass backward for short key sequences:
 // every key of a (b, h) fits one workgroup (Nk <= 224, d = 64 or 96), as in
-// the global-attention stages of Hiera at 224^2 (196 and 49 tokens, "Hiera: A
-// Hierarchical Vision Transformer without the Bells-and-Whistles", Sec. 3).
-// Any mask.
+// the global-attention stages of Hiera-Base at 224x224 ("hiera-optim 0.1.0",
+// Results, and the sdist's mask_unit.py on the global-attention stages; the
+// 14x14 grid has 196 tokens).  Any mask.
 //
 // The backward of FlashAttention-2 ("IHA-CUDA", Repository Structure:
 // preprocess, flash backward, postprocess) needs three passes over HBM when

@@ -197,9 +197,9 @@ enum attn_pass {
  *      dK/dV waves and its dQ waves run the two backward passes side by
  *      side.  attn_bwd_passes then accepts only ATTN_PASS_ALL.
  *   2  otherwise, bf16 or fp16 with d = 64 or 96, Nk <= 224 and Nq <= 1024,
- *      any mask (the global-attention stages of Hiera at 224^2 have 196 and
- *      49 tokens: "Hiera: A Hierarchical Vision Transformer without the
- *      Bells-and-Whistles", Sec. 3): one workgroup holds every key of a
+ *      any mask (the global-attention stages of Hiera-Base at 224x224 --
+ *      "hiera-optim 0.1.0", Results and sdist mask_unit.py -- of which the
+ *      14x14 grid has 196 tokens): one workgroup holds every key of a
  *      (b, h) and loops over its query rows.  attn_bwd_passes with
  *      ATTN_PASS_ALL runs the fused kernel; a partial pass set runs the
  *      general passes.

@@ -3,9 +3,9 @@ returns 2: at most 224 keys and 1024 query rows, d = 64 or 96, 16-bit): one
 workgroup per (b, h) holds every key, so the row sums D_i, dK/dV and dQ come
 out of one pass over HBM.  Against the fp64 oracle on the same seeded inputs,
 for every mask, ragged key blocks (Nk not a multiple of 32) and query slabs
-(Nq not a multiple of 32), Nq != Nk, and the Hiera global-attention token
-counts (196 and 49 tokens: "Hiera: A Hierarchical Vision Transformer without
-the Bells-and-Whistles", Sec. 3 -- stages 3 and 4 at 224^2).  The same
+(Nq not a multiple of 32), Nq != Nk, and global-attention token counts of
+Hiera-Base at 224x224 ("hiera-optim 0.1.0", Results: the 14x14 grid's 196
+tokens, and 49 for a 7x7 grid).  The same
 geometry through the three general passes, called one at a time, is checked
 too: it stays reachable for callers that time or schedule the passes."""
 import pytest
