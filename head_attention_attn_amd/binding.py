@@ -99,6 +99,8 @@ def load_library():
     lib.attn_check_premix_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp, vp, vp, vp, fp,
                                           vp, ctypes.c_size_t]
     lib.attn_check_premix_bwd.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = lib.attn_bwd.argtypes[:-3] + [vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -311,6 +313,37 @@ def bwd(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
         st = lib.attn_bwd_strided(*args, ctypes.byref(L), _stream(q))
     if st != 0:
         raise AttnError(st, "attn_bwd_passes")
+    return dq, dk, dv
+
+
+# size of the library's scratch array for attn_bwd_noalloc (include/attn.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def bwd_noalloc(q, k, v, o, lse, do, mask: str = "none", window: int = 0, scale=None,
+                dq=None, dk=None, dv=None):
+    """``attn_bwd_noalloc``: the backward with the row sums in the library's
+    own device scratch array, so the call itself allocates nothing (outputs
+    given by the caller are written in place; missing ones are allocated
+    here).  Contiguous [B, H, N, d] tensors only.  Raises AttnError
+    (ATTN_ERR_WORKSPACE) when 4 B H Nq bytes exceed the scratch array."""
+    lib = load_library()
+    B, H, Nq, Nk, d, mask, window = _geometry(q, k, v, *_mask_args(q, mask, window))
+    _check_out(o, q, "o")
+    _check_out(do, q, "do")
+    _check_lse(lse, B, H, Nq, q.device)
+    dq = _empty_rows(q) if dq is None else _check_out(dq, q, "dq")
+    dk = _empty_rows(k) if dk is None else _check_out(dk, k, "dk")
+    dv = _empty_rows(v) if dv is None else _check_out(dv, v, "dv")
+    if not _is_plain(q, k, v, o, do, dq, dk, dv):
+        raise ValueError("attn_bwd_noalloc takes contiguous [B, H, N, d] tensors only")
+    st = lib.attn_bwd_noalloc(DTYPE_CODES[q.dtype], B, H, Nq, Nk, d, _scale(scale, d),
+                              MASK_CODES[mask], window, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), _stream(q))
+    if st != 0:
+        raise AttnError(st, f"attn_bwd_noalloc ({workspace_bytes(B, H, Nq)} bytes of row sums, "
+                            f"scratch holds {NOALLOC_SCRATCH_BYTES})")
     return dq, dk, dv
 
 

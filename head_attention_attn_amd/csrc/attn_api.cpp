@@ -1,7 +1,9 @@
 // attn_api.cpp -- the C ABI of include/attn.h: argument validation, device
 // gating and dispatch to the kernel launchers.  No device memory is allocated
-// here and no state is kept per call; the only global state is a per-device
-// cache of "is this a gfx950", filled once under a mutex.
+// here and no state is kept per call; the global state is a per-device cache
+// of "is this a gfx950" and, for attn_bwd_noalloc, a static device scratch
+// array with a per-device cache of its address, both filled once under a
+// mutex.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -17,6 +19,12 @@ static_assert(int(ATTN_PASS_ROWSUM) == int(attn::kPassRowSum) &&
                   int(ATTN_PASS_DKDV) == int(attn::kPassDKDV) &&
                   int(ATTN_PASS_DQ) == int(attn::kPassDQ) && int(ATTN_PASS_ALL) == int(attn::kPassAll),
               "pass bits of attn.h and the launchers agree");
+
+// Scratch of attn_bwd_noalloc: device memory that the library holds (one
+// copy per GPU, until the process ends) for callers that cannot allocate.  In
+// host code `scratch` names a host-side stand-in, not the device array: host
+// code uses only the device address that scratch_ptr() looks up.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -82,6 +90,23 @@ int check_device() {
     arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
   }
   return arch_ok[dev] == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU holds its own copy at its own
+// address); null if the lookup fails.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
 }
 
 attn::MaskGeom make_geom(int mask, int64_t Nq, int64_t Nk, int64_t window) {
@@ -568,6 +593,23 @@ int attn_bwd(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
              void* workspace, size_t workspace_bytes, void* stream) {
   return attn_bwd_passes(ATTN_PASS_ALL, dtype, B, H, Nq, Nk, d, scale, mask, window, q, k, v, o,
                          lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_noalloc(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                     float scale, int mask, int64_t window, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                     void* dk, void* dv, void* stream) {
+  int st = check_geometry(dtype, B, H, Nq, Nk, d, scale, mask, window);
+  if (st) return st;
+  // the minimum workspace: row sums only, so the dQ pass recomputes
+  const size_t need = ws_size(B, H, Nq);
+  if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+  st = check_device();
+  if (st) return st;
+  void* ws = scratch_ptr();
+  if (!ws) return ATTN_ERR_DEVICE;
+  return attn_bwd(dtype, B, H, Nq, Nk, d, scale, mask, window, q, k, v, o, lse, dout, dq, dk, dv,
+                  ws, need, stream);
 }
 
 // ------------------------------------------------------------ IHA premix

@@ -397,6 +397,29 @@ ATTN_API int attn_check_premix_bwd(int dtype, int64_t B, int64_t N, int64_t H, i
                                    const void* dx, const float* dw, const void* workspace,
                                    size_t workspace_bytes);
 
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace.  The row sums D go to
+ * a scratch array that the library holds in device memory: one copy per GPU,
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes, held until the process ends.  Calls whose
+ * minimum workspace, attn_bwd_workspace_size(B, H, Nq) = 4 B H Nq bytes
+ * rounded up to 256, exceeds that size return ATTN_ERR_WORKSPACE and enqueue
+ * nothing (B H Nq <= 4,194,304 rows fit).  The call allocates nothing and
+ * records no memset: the row-sum pass writes every D it reads, and the dQ
+ * pass recomputes S and dP (no kept dS).  Results equal attn_bwd's with a
+ * workspace of attn_bwd_workspace_size(B, H, Nq) bytes.  Every call on one GPU
+ * shares that GPU's scratch array, which keeps the last call's contents:
+ * calls that overlap on one GPU (two streams, or two threads) race on it and
+ * must be ordered by the caller.  Errors as attn_bwd.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+ATTN_API int attn_bwd_noalloc(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                              float scale, int mask, int64_t window,
+                              const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout,
+                              void* dq, void* dk, void* dv, void* stream);
+
 /* attn_status_string -- static, human-readable name of a status code. */
 ATTN_API const char* attn_status_string(int status);
 

@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
                                          "attn_bwd_strided", "attn_check_fwd_strided",
                                          "attn_check_bwd_strided", "attn_premix_fwd",
                                          "attn_premix_bwd", "attn_premix_bwd_workspace_size",
-                                         "attn_check_premix_fwd", "attn_check_premix_bwd"])
+                                         "attn_check_premix_fwd", "attn_check_premix_bwd",
+                                         "attn_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -278,3 +279,25 @@ def test_size_limits(lib):
     assert chk(1, (1 << 24) + 16, 64, 128) == INVALID         # d = 128: 2^24 rows is the bound
     assert chk(4, 1 << 24, 1 << 24, 64, mask=2, window=64) == OK   # 2^32 elements per tensor
     assert chk(1, (1 << 30) + 1, 64, 64) == INVALID           # row count past 2^30
+
+
+def test_noalloc_rejects_rows_beyond_its_scratch(lib):
+    """attn_bwd_noalloc keeps the row sums in a 16 MiB array of its own: a
+    call needing more (4 B H Nq bytes, rounded up to 256) is refused with
+    ATTN_ERR_WORKSPACE before any pointer or device is touched; geometry
+    errors come first, as in attn_bwd."""
+    f = lib.attn_bwd_noalloc
+    args = lambda B, H, Nq, d=128: (BF16, B, H, Nq, Nq, d, 0.125, MASK["causal"], 0) + (None,) * 9 + (None,)
+    assert f(*args(1, 1, 4 * 1024 * 1024 + 1)) == WORKSPACE
+    assert f(*args(2, 8, 300000)) == WORKSPACE
+    assert f(*args(1, 1, 1000, d=80)) == UNSUPPORTED
+    assert f(*args(0, 1, 1000)) == INVALID
+    # the largest accepted row count needs exactly the scratch size
+    assert lib.attn_bwd_workspace_size(1, 1, 4 * 1024 * 1024) == binding.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_workspace_size(1, 1, 4 * 1024 * 1024 + 1) > binding.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_is_not_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.lib_path()],
+                         capture_output=True, text=True).stdout
+    assert not [l for l in out.splitlines() if "scratch" in l]
