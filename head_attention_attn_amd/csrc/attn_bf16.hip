@@ -510,7 +510,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int i0 = t0 + j * BQ;
     return wlo < whi && i0 < whi && i0 + BQ > wlo;
   };
-  const int hoff = (kb * 2 * 64 + lane) * 8;  // this lane's 16 bytes of chunk 0 in a P / dS buffer
 
   if (ntiles > 0) {
     fetch(0);
@@ -527,53 +526,79 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     V8 kop[KC], vop[KC];
     load_operand_rows<D, E>(kop, K + rrow<SR, D>(a.rk, myk), kvalid, gq);
     load_operand_rows<D, E>(vop, V + rrow<SR, D>(a.rv, myk), kvalid, gq);
-    const int clo = kvalid ? mg.col_lo(myk) : 0;
-    const int chi = kvalid ? mg.col_hi(myk) : 0;
     const float sl2 = a.scale * kLog2e;
 
+    // kept dS blocks of this key block: the (b, h) base plus the blocks of
+    // the key blocks before it
+    uint16_t* dsb = a.ds;
+    int64_t ds0 = 0;
+    if (a.ds) {
+      dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
+      ds0 = ds_offset(mg, wk0 / 32, lane);
+    }
     auto produce = [&](const uint16_t* q_l, const uint16_t* g_l, const float* s_l,
                        uint16_t* p_l, uint16_t* d_l, int j) {
       if (!sees(j)) return;
       const int i0 = t0 + j * BQ;
       const bool full = wk1 == wk0 + 32 && mg.tile_full(i0, i0 + BQ, wk0, wk1);
-      // S first, then dP: P = exp2(...) depends on S only and overlaps the
-      // dP products still in the matrix pipe
+      // Transposed products S^T = K Q^T and dP^T = V dO^T: lane l holds
+      // query i0 + l % 32, its 16 entries keys 8 (e / 4) + 4 (l / 32) + e % 4
+      // of the block, so lse and D are one value per lane and dS^T leaves the
+      // accumulator already in the dQ pass's operand order.  Operand reads
+      // run ahead of the products that use them (the order is pinned by
+      // scheduling fences); S first, then dP: P = exp2(...) depends on S only
+      // and overlaps the dP products still in the matrix pipe.
+      V8 qa[KC], ga[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qa[kc] = lds_row8<D, E>(q_l, 0, lane & 31, kc, gq);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) s = mfma32<E>(lds_row8<D, E>(q_l, 0, lane & 31, kc, gq), kop[kc], s);
+      for (int kc = 0; kc < KC; ++kc) {
+        s = mfma32<E>(kop[kc], qa[kc], s);
+        ga[kc] = lds_row8<D, E>(g_l, 0, lane & 31, kc, gq);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) dp = mfma32<E>(lds_row8<D, E>(g_l, 0, lane & 31, kc, gq), vop[kc], dp);
+      for (int kc = 0; kc < KC; ++kc) dp = mfma32<E>(vop[kc], ga[kc], dp);
+      const float lq = s_l[lane & 31];       // lse * log2(e) of this lane's query
+      const float dq = s_l[32 + (lane & 31)];  // D of this lane's query
       with_mask(!full, [&](auto masked) {
+        // keys visible to this lane's query (none past the last row)
+        const int qi = i0 + (lane & 31);
+        const int rlo = qi < a.nq ? mg.row_lo(qi) : 0, rhi = qi < a.nq ? mg.row_hi(qi) : 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&s_l[8 * i + 4 * gq]);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int e = 4 * i + jj;
-            float arg = fmaf(s[e], sl2, -L4[jj]);
-            if constexpr (decltype(masked)::value) {
-              const int qi = i0 + 8 * i + 4 * gq + jj;
-              arg = ((qi >= clo) & (qi < chi)) ? arg : -INFINITY;
-            }
-            s[e] = fast_exp2(arg);
+        for (int e = 0; e < 16; ++e) {
+          float arg = fmaf(s[e], sl2, -lq);
+          if constexpr (decltype(masked)::value) {
+            const int kj = wk0 + 8 * (e >> 2) + 4 * gq + (e & 3);
+            arg = ((kj >= rlo) & (kj < rhi)) ? arg : -INFINITY;
           }
+          s[e] = fast_exp2(arg);
         }
       });
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&s_l[32 + 8 * i + 4 * gq]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) dp[4 * i + jj] = s[4 * i + jj] * (dp[4 * i + jj] - D4[jj]);
-      }
-      // P in register order; dS as a [key][query] 32 x 32 tile (ds_tile_off)
+      for (int e = 0; e < 16; ++e) dp[e] = s[e] * (dp[e] - dq);
+      // P^T and dS^T as [query][key] 32 x 32 tiles (ds_tile_off); the
+      // accumulate waves read them transposed
+      uint16_t* pt = p_l + kb * 1024;
       uint16_t* dt = d_l + kb * 1024;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        *reinterpret_cast<V8*>(p_l + hoff + c * 512) = acc_chunk<E>(s, c);
+        const V8 pv = acc_chunk<E>(s, c);
         const V8 v = acc_chunk<E>(dp, c);
+        *reinterpret_cast<V4*>(pt + ds_tile_off(lane & 31, 4 * c + gq)) = V4{pv[0], pv[1], pv[2], pv[3]};
+        *reinterpret_cast<V4*>(pt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) = V4{pv[4], pv[5], pv[6], pv[7]};
         *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + gq)) = V4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) =
-            V4{v[4], v[5], v[6], v[7]};
+        *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) = V4{v[4], v[5], v[6], v[7]};
+        if (a.ds) {
+          // keep the block for the dQ pass straight from the registers: chunk
+          // c of block i0 / 32 - wlo / 32 of this key block's ds_count() (in
+          // range because sees(j) holds), streamed past the caches like the
+          // output tiles
+          uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(blk + (c * 64 + lane) * 8));
+        }
       }
     };
 
@@ -609,42 +634,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       dkacc[db] = f32x16{};
       dvacc[db] = f32x16{};
     }
-    // kept dS blocks of this key block: the (b, h) base plus the blocks of
-    // the key blocks before it
-    uint16_t* dsb = a.ds;
-    int64_t ds0 = 0;
-    if (a.ds) {
-      dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
-      ds0 = ds_offset(mg, wk0 / 32, lane);
-    }
     auto consume = [&](const uint16_t* q_l, const uint16_t* g_l, const uint16_t* p_l,
                        const uint16_t* d_l, int j) {
       if (!sees(j)) return;
-      if (a.ds) {
-        // keep the block for the dQ pass, already in its MFMA operand order
-        // (lane = query, 8 keys of a 16-key chunk per lane): 2 x 1 KB,
-        // streamed past the caches like the output tiles.  Block
-        // i0 / 32 - wlo / 32 of this key block's ds_count(): in range because
-        // sees(j) holds (a nonempty query range overlapping the tile).
-        const int i0 = t0 + j * BQ;
-        uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, lds_tr8_ds<E>(d_l + kb * 1024, 16 * cc, 0, lane)),
-                                      reinterpret_cast<u32x4*>(blk + (cc * 64 + lane) * 8));
-      }
+      // P and dS operands (lane = key, 8 queries of a 16-row chunk) by
+      // transposed reads of the [query][key] tiles
+      const uint16_t* pt = p_l + kb * 1024;
       const uint16_t* dt = d_l + kb * 1024;
+      // operand reads run kLead products ahead of the product that uses them
+      // (the order is pinned by scheduling fences): product i of the 2 DB
+      // products per 16-row chunk c is dV (even i) or dK (odd i) of block
+      // db = (i / 2) % DB
+      constexpr int NP = 4 * DB, kLead = 8;
+      V8 pop[2], dsop[2], op[NP];
+      auto opread = [&](int i) {
+        const int c = i / (2 * DB), db = (i / 2) % DB;
+        op[i] = lds_tr8<D, E>((i & 1) ? q_l : g_l, 16 * c, 32 * db, lane);
+      };
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const V8 pop = *reinterpret_cast<const V8*>(p_l + hoff + c * 512);
-        const V4 d0 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * c + gq));
-        const V4 d1 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * c + 2 + gq));
-        const V8 dsop = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        pop[c] = lds_tr8_ds<E>(pt, 16 * c, 0, lane);
+        dsop[c] = lds_tr8_ds<E>(dt, 16 * c, 0, lane);
+      }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dvacc[db] = mfma32<E>(lds_tr8<D, E>(g_l, 16 * c, 32 * db, lane), pop, dvacc[db]);
-          dkacc[db] = mfma32<E>(lds_tr8<D, E>(q_l, 16 * c, 32 * db, lane), dsop, dkacc[db]);
-        }
+      for (int i = 0; i < kLead; ++i) opread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int c = i / (2 * DB), db = (i / 2) % DB;
+        if (i & 1)
+          dkacc[db] = mfma32<E>(op[i], dsop[c], dkacc[db]);
+        else
+          dvacc[db] = mfma32<E>(op[i], pop[c], dvacc[db]);
+        if (i + kLead < NP) opread(i + kLead);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (ntiles > 0) {
