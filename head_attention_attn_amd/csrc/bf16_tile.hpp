@@ -174,16 +174,21 @@ struct RegTile {
   static constexpr int CPR = D / 8, TOTAL = ROWS * CPR, CH = (TOTAL + NT - 1) / NT;
   uint4 r[CH];
 
+  // a uniform base (contiguous rows: the tile's first row) plus a 32-bit
+  // per-lane byte offset, the scalar-base form of the load (one address
+  // register per load and no 64-bit address arithmetic per lane)
   template <bool SR>
   __device__ __forceinline__ void load(const uint16_t* src, const RowMap& rm, int r0, int n,
                                        int tid) {
+    const char* base = reinterpret_cast<const char*>(SR ? src : src + (int64_t)r0 * D);
+    const int last = SR ? n - 1 : n - 1 - r0;
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
       const int c = tid + t * NT;
       if (TOTAL % NT == 0 || c < TOTAL) {
-        const int row = min(r0 + c / CPR, n - 1);
-        r[t] = *reinterpret_cast<const uint4*>(src + (SR ? (int64_t)rm.row(row) : (int64_t)row * D) +
-                                               (c % CPR) * 8);
+        const int row = min((SR ? r0 : 0) + c / CPR, last);
+        const uint32_t off = 2u * ((SR ? rm.row(row) : (uint32_t)row * D) + (uint32_t)(c % CPR) * 8);
+        r[t] = *reinterpret_cast<const uint4*>(base + off);
       }
     }
   }
