@@ -536,9 +536,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
       ds0 = ds_offset(mg, wk0 / 32, lane);
     }
+    uint16_t* kept = nullptr;  // kept dS block of the step's tile, if any
+    V8 kv[2];
     auto produce = [&](const uint16_t* q_l, const uint16_t* g_l, const float* s_l,
                        uint16_t* p_l, uint16_t* d_l, int j) {
-      if (!sees(j)) return;
+      kept = nullptr;
+      if (j >= ntiles || !sees(j)) return;
       const int i0 = t0 + j * BQ;
       const bool full = wk1 == wk0 + 32 && mg.tile_full(i0, i0 + BQ, wk0, wk1);
       // Transposed products S^T = K Q^T and dP^T = V dO^T: lane l holds
@@ -591,35 +594,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
         *reinterpret_cast<V4*>(pt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) = V4{pv[4], pv[5], pv[6], pv[7]};
         *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + gq)) = V4{v[0], v[1], v[2], v[3]};
         *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) = V4{v[4], v[5], v[6], v[7]};
-        if (a.ds) {
-          // keep the block for the dQ pass straight from the registers: chunk
-          // c of block i0 / 32 - wlo / 32 of this key block's ds_count() (in
-          // range because sees(j) holds), streamed past the caches like the
-          // output tiles
-          uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(blk + (c * 64 + lane) * 8));
-        }
+      }
+      if (a.ds) {
+        // the block kept for the dQ pass: block i0 / 32 - wlo / 32 of this
+        // key block's ds_count() (in range because sees(j) holds)
+        kept = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
+        kv[0] = acc_chunk<E>(dp, 0);
+        kv[1] = acc_chunk<E>(dp, 1);
+      }
+    };
+    // End of a step: wait for the rows fetched at its start, then store the
+    // kept dS block straight from the registers, streamed past the caches
+    // like the output tiles.  The wait sits on every path, ahead of the
+    // stores, so the next step's put finds the staged rows retired instead
+    // of waiting for these stores as well.
+    auto keep = [&]() {
+      wait_vmem();
+      if (kept) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, kv[c]),
+                                      reinterpret_cast<u32x4*>(kept + (c * 64 + lane) * 8));
       }
     };
 
     if (ntiles > 0) {
       __syncthreads();
       produce(sQ0, sG0, sS0, sP0, sD0, 0);
+      keep();
       __syncthreads();
     }
     // step j: load tile j + 2, produce tile j + 1 (the accumulate waves
-    // consume tile j meanwhile), barrier
+    // consume tile j meanwhile), keep its dS, barrier
     for (int j = 0; j < ntiles; j += 3) {
       if (j + 2 < ntiles) load(sQ2, sG2, sS2, j + 2);
-      if (j + 1 < ntiles) produce(sQ1, sG1, sS1, sP1, sD1, j + 1);
+      produce(sQ1, sG1, sS1, sP1, sD1, j + 1);
+      keep();
       __syncthreads();
       if (j + 1 >= ntiles) break;
       if (j + 3 < ntiles) load(sQ0, sG0, sS0, j + 3);
-      if (j + 2 < ntiles) produce(sQ2, sG2, sS2, sP2, sD2, j + 2);
+      produce(sQ2, sG2, sS2, sP2, sD2, j + 2);
+      keep();
       __syncthreads();
       if (j + 2 >= ntiles) break;
       if (j + 4 < ntiles) load(sQ1, sG1, sS1, j + 4);
-      if (j + 3 < ntiles) produce(sQ0, sG0, sS0, sP0, sD0, j + 3);
+      produce(sQ0, sG0, sS0, sP0, sD0, j + 3);
+      keep();
       __syncthreads();
     }
     // staging barriers of the accumulate waves' epilogue

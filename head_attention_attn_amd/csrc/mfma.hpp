@@ -83,6 +83,14 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0): wait until every vector memory load and store of the
+// wave has retired (export and LDS counters untouched).  On gfx950 loads and
+// stores share that one counter, so where a register-staged load is followed
+// by stores on some paths only, the compiler's own wait at the load's use has
+// to assume the stores and waits for them too; waiting here, before the
+// stores, leaves nothing outstanding on the staged registers.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // x on lane l combined with x on lane l ^ 32 (the same row's other half in
 // the MFMA accumulator layout).  v_permlane32_swap of x with itself leaves
 // the lower-half value in one result and the upper-half value in the other
