@@ -22,8 +22,8 @@
 // backward, postprocess dQaccum -> dQ), restructured as three deterministic
 // passes with no atomics:
 //   dsum:  D_i = sum_c dO[i][c] * O[i][c]                       (fp32)
-//   dK/dV: workgroup per block of 32*NW keys; each wave owns 32 keys (lane
-//          columns) and loops over the visible 32-query tiles in LDS:
+//   dK/dV: workgroup per block of keys, looping over the visible query
+//          tiles in LDS:
 //            S = Q K^T, dP = dO V^T, P = exp(S*scale - lse), dS = P*(dP - D)
 //            dV^T += dO^T P,  dK^T += Q^T dS   (dO^T, Q^T by transpose reads)
 //   dQ:    workgroup per block of 32*NW queries; loops over visible 64-key
@@ -420,27 +420,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   }
 }
 
-// dK/dV pass at D = 128: a workgroup of 8 waves (two per SIMD) for 128 keys,
-// in two roles working one query tile apart.
-//   score waves 0..3 (key block w): K, V rows of the block as register
-//     operands; per 32-query tile S = Q K^T, dP = dO V^T, P = exp(S*scale -
-//     lse), dS = P (dP - D), rounded to bf16 and handed over through LDS (P in
-//     the accumulator's register order, 16 bytes per lane per 16-row chunk;
-//     dS as a [key][query] tile, 8-byte chunks swizzled by ds_tile_off);
-//   accumulate waves 4..7 (key block w - 4): dV^T += dO^T P, dK^T += Q^T dS
-//     with dO^T, Q^T from transpose reads of the same Q / dO tiles; when the
-//     caller gave room they also write each dS tile to the workspace for the
-//     dQ pass (the score waves carry the longer dependency chain per step).
-// Each role's live registers stay under the two-waves-per-SIMD budget, and
-// a score wave's softmax arithmetic overlaps its partner's MFMAs.  Q / dO
-// tiles cycle through three named buffers (one being loaded, one read by the
-// score waves, one by the accumulate waves), P / dS through three more.
+// dK/dV pass at D = 128: a workgroup of 16 waves (four per SIMD) for 128
+// keys, in two roles working one query tile apart.
+//   score waves 0..7: the two waves of key block kb = w / 2 hold its 32 K and
+//     V rows as register operands, and wave w takes query rows 16 (w % 2) ..
+//     + 15 of each 32-row Q / dO tile: the transposed products S^T = K Q^T
+//     and dP^T = V dO^T as 16 x 16 blocks (v_mfma_f32_16x16x32; lane l:
+//     query 16 (w % 2) + l % 16, keys 4 (l / 16) .. + 3 of each 16-key
+//     half), P = exp(S*scale - lse) and dS = P (dP - D), rounded to E and
+//     handed over as its rows of the key block's [query][key] P and dS tiles
+//     (8-byte chunks swizzled by ds_tile_off); the score waves also load the
+//     Q / dO tiles and the row statistics;
+//   accumulate waves 8..15: wave 8 + m owns key block m / 2 and head-dim half
+//     m % 2: dV^T += dO^T P, dK^T += Q^T dS with 32x32x16 products, dO^T, Q^T
+//     and the P, dS operands from transpose reads; when the caller gave room,
+//     wave m % 2 of a key block also writes 16-key chunk m % 2 of each dS
+//     block to the workspace, in the dQ pass's operand order.
+// Splitting a key block's softmax arithmetic over two score waves halves the
+// dependency chain each carries per step (one wave per key block carried the
+// whole 32 x 32 tile before: 849 -> 781 us on the causal workload), with the
+// same LDS operand traffic: a score wave reads only its 16 query rows, each
+// read feeding the products of both key halves.  Q / dO tiles cycle through
+// three named buffers (one being loaded, one read by the score waves, one by
+// the accumulate waves), P / dS through three more.
 template <typename E, int D, int MODE, bool SR>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void dkdv_pp_kernel(BwdArgs a, int nkt) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void dkdv_k16_kernel(BwdArgs a, int nkt) {
   using V8 = typename E::v8;
   using V4 = typename E::v4;
-  constexpr int NT = 512, BK = 128, BQ = 32, TE = tile_elems<BQ, D>();
-  constexpr int KC = D / 16, DB = D / 32, PE = 4 * 2 * 64 * 8;  // 4 blocks x 2 chunks x 64 lanes x 16 B
+  static_assert(D == 128, "16-key score waves: d = 128");
+  constexpr int NS = 512, BK = 128, BQ = 32, TE = tile_elems<BQ, D>();
+  constexpr int KS = D / 32, PE = 4 * 2 * 64 * 8;  // 4 blocks x 2 chunks x 64 lanes x 16 B
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sG0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sQ1[TE];
@@ -461,12 +470,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int wave = wave_id(tid);
   const int BH = a.B * a.H;
   MaskGeom mg = a.mg;
-  if (MODE != kAnyMask) mg.mode = MODE;  // compile-time mask mode: visibility folds to one case
+  if (MODE != kAnyMask) mg.mode = MODE;
   // causal: low key tiles see the most queries
   const TileId tix = tile_of(blockIdx.x, BH, nkt, mg.mode == kCausal, false);
   const int bh = tix.bh, kt = tix.t;
   const int k0 = kt * BK, k1 = min(k0 + BK, a.nk);
-  const int kb = wave & 3;                 // key block of this wave (either role)
+  const int kb = (wave & 7) >> 1;          // key block of this wave (either role)
   const int wk0 = k0 + 32 * kb, wk1 = min(wk0 + 32, a.nk);
 
   const uint16_t* Q = (const uint16_t*)a.q + rslice<SR, D>(a.rq, bh, a.H, a.nq);
@@ -479,31 +488,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   if (wk0 < a.nk) mg.query_range(wk0, wk1, &wlo, &whi);
   const int t0 = range_tile_row(lo, BQ, 0);
   const int ntiles = lo < hi ? (hi - t0 + BQ - 1) / BQ : 0;
-
-  // Q / dO / lse / D of tile j are fetched into registers one step before
-  // they are written to LDS (fetch(j + 3) is issued right after put(j + 2))
-  RegTile<BQ, D, NT> rq, rg;
-  float rstat = 0.f;
-  auto fetch = [&](int j) {
-    const int r0 = t0 + j * BQ;
-    rq.template load<SR>(Q, a.rq, r0, a.nq, tid);
-    rg.template load<SR>(dO, a.rdo, r0, a.nq, tid);
-    // every lane loads (no branch around a load: a value loaded under a
-    // divergent branch is waited for where the branch rejoins, which would
-    // cancel the prefetch); only threads 0..63 store theirs
-    const int t = tid & 63;
-    rstat = (t < 32 ? LSE : DS)[min(r0 + (t & 31), a.nq - 1)];
-  };
-  auto put = [&](uint16_t* q_l, uint16_t* g_l, float* s_l) {
-    rq.store(q_l, tid);
-    rg.store(g_l, tid);
-    if (tid < 64) s_l[tid] = tid < 32 ? rstat * kLog2e : rstat;  // lse in log2 units
-  };
-  // put tile j into a set and fetch tile j + 1 into the registers
-  auto load = [&](uint16_t* q_l, uint16_t* g_l, float* s_l, int j) {
-    put(q_l, g_l, s_l);
-    if (j + 1 < ntiles) fetch(j + 1);
-  };
   // does this wave's key block see any row of tile j (an empty query range
   // [wlo, whi) sees none)
   auto sees = [&](int j) {
@@ -511,135 +495,155 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     return wlo < whi && i0 < whi && i0 + BQ > wlo;
   };
 
-  if (ntiles > 0) {
-    fetch(0);
-    load(sQ0, sG0, sS0, 0);
-  }
-  if (ntiles > 1) load(sQ1, sG1, sS1, 1);
-
-  if (wave < 4) {
+  if (wave < 8) {
     // ---------------------------------------------------------- score waves
+    // Q / dO / lse / D of tile j are fetched into registers one step before
+    // they are written to LDS (fetch(j + 3) is issued right after put(j + 2))
+    RegTile<BQ, D, NS> rq, rg;
+    float rstat = 0.f;
+    auto fetch = [&](int j) {
+      const int r0 = t0 + j * BQ;
+      rq.template load<SR>(Q, a.rq, r0, a.nq, tid);
+      rg.template load<SR>(dO, a.rdo, r0, a.nq, tid);
+      // every lane loads (no branch around a load: a value loaded under a
+      // divergent branch is waited for where the branch rejoins, which would
+      // cancel the prefetch); only threads 0..63 store theirs
+      const int t = tid & 63;
+      rstat = (t < 32 ? LSE : DS)[min(r0 + (t & 31), a.nq - 1)];
+    };
+    // lane offsets, re-read each step (opaque to loop-invariant hoisting,
+    // which would keep one address register per buffer set and read and
+    // spill): this thread's 16 bytes of a staged tile, the B operand reads
+    // (plus 32 ks per head-dim chunk) and the P / dS writes of key half kh
+    const int qh = wave & 1;                 // query half of the tile: rows 16 qh .. + 15
+    const int g4 = lane >> 4;                // key group: keys 4 g4 .. + 3 of a 16-key half
+    const int r = 16 * qh + (lane & 15);     // this lane's tile row
+    static_assert(BQ * D / 8 == NS, "one 16-byte piece of a staged tile per thread");
+    int poff = toff<D>(tid / (D / 8), (tid % (D / 8)) * 8);
+    int roff = toff2<D>(16 * qh, lane & 15, 0, 8 * g4);
+    int woff[2] = {kb * 1024 + ds_tile_off(r, g4), kb * 1024 + ds_tile_off(r, 4 + g4)};
+    int soff = tid;
+    auto opaque = [&]() {
+      asm volatile("" : "+v"(poff), "+v"(roff), "+v"(woff[0]), "+v"(woff[1]), "+v"(soff));
+    };
+    auto put = [&](uint16_t* q_l, uint16_t* g_l, float* s_l) {
+      opaque();
+      *reinterpret_cast<uint4*>(q_l + poff) = rq.r[0];
+      *reinterpret_cast<uint4*>(g_l + poff) = rg.r[0];
+      if (tid < 64) s_l[soff] = tid < 32 ? rstat * kLog2e : rstat;  // lse in log2 units
+    };
+    // put tile j into a set and fetch tile j + 1 into the registers
+    auto load = [&](uint16_t* q_l, uint16_t* g_l, float* s_l, int j) {
+      put(q_l, g_l, s_l);
+      if (j + 1 < ntiles) fetch(j + 1);
+    };
+    if (ntiles > 0) {
+      fetch(0);
+      load(sQ0, sG0, sS0, 0);
+    }
+    if (ntiles > 1) load(sQ1, sG1, sS1, 1);
+
     const uint16_t* K = (const uint16_t*)a.k + rslice<SR, D>(a.rk, bh, a.H, a.nk);
     const uint16_t* V = (const uint16_t*)a.v + rslice<SR, D>(a.rv, bh, a.H, a.nk);
-    const int myk = wk0 + (lane & 31);
-    const bool kvalid = myk < a.nk;
-    V8 kop[KC], vop[KC];
-    load_operand_rows<D, E>(kop, K + rrow<SR, D>(a.rk, myk), kvalid, gq);
-    load_operand_rows<D, E>(vop, V + rrow<SR, D>(a.rv, myk), kvalid, gq);
+    // A operands (16 keys x 32 head dims per product): for key half kh, lane
+    // l holds key wk0 + 16 kh + l % 16, dims 32 ks + 8 (l / 16) .. + 7
+    V8 kop[2][KS], vop[2][KS];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int myk = wk0 + 16 * kh + (lane & 15);
+      const bool kvalid = myk < a.nk;
+      const uint16_t* kr = K + rrow<SR, D>(a.rk, kvalid ? myk : 0);
+      const uint16_t* vr = V + rrow<SR, D>(a.rv, kvalid ? myk : 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kop[kh][ks] = kvalid ? *reinterpret_cast<const V8*>(kr + 32 * ks + 8 * g4) : V8{};
+        vop[kh][ks] = kvalid ? *reinterpret_cast<const V8*>(vr + 32 * ks + 8 * g4) : V8{};
+      }
+    }
     const float sl2 = a.scale * kLog2e;
 
-    // kept dS blocks of this key block: the (b, h) base plus the blocks of
-    // the key blocks before it
-    uint16_t* dsb = a.ds;
-    int64_t ds0 = 0;
-    if (a.ds) {
-      dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
-      ds0 = ds_offset(mg, wk0 / 32, lane);
-    }
-    uint16_t* kept = nullptr;  // kept dS block of the step's tile, if any
-    V8 kv[2];
     auto produce = [&](const uint16_t* q_l, const uint16_t* g_l, const float* s_l,
                        uint16_t* p_l, uint16_t* d_l, int j) {
-      kept = nullptr;
-      if (j >= ntiles || !sees(j)) return;
+      if (!sees(j)) return;
+      opaque();
       const int i0 = t0 + j * BQ;
-      const bool full = wk1 == wk0 + 32 && mg.tile_full(i0, i0 + BQ, wk0, wk1);
-      // Transposed products S^T = K Q^T and dP^T = V dO^T: lane l holds
-      // query i0 + l % 32, its 16 entries keys 8 (e / 4) + 4 (l / 32) + e % 4
-      // of the block, so lse and D are one value per lane and dS^T leaves the
-      // accumulator already in the dQ pass's operand order.  Operand reads
-      // run ahead of the products that use them (the order is pinned by
-      // scheduling fences); S first, then dP: P = exp2(...) depends on S only
-      // and overlaps the dP products still in the matrix pipe.
-      V8 qa[KC], ga[KC];
+      const bool full = wk1 == wk0 + 32 && mg.tile_full(i0 + 16 * qh, i0 + 16 * qh + 16, wk0, wk1);
+      // read i: the B operand (32 dims x 16 queries) of head-dim chunk
+      // i % 4, a row read of the Q (i < 4) or dO tile: lane l holds query
+      // 16 qh + l % 16, dims 32 (i % 4) + 8 (l / 16) .. + 7; each read feeds
+      // the products of both key halves.  Reads run kLead ahead.
+      constexpr int NR = 2 * KS, kLead = 2;
+      V8 op[NR];
+      auto rd = [&](int i) {
+        op[i] = *reinterpret_cast<const V8*>((i < KS ? q_l : g_l) + roff + 32 * (i % KS));
+      };
+      f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) qa[kc] = lds_row8<D, E>(q_l, 0, lane & 31, kc, gq);
+      for (int i = 0; i < kLead; ++i) rd(i);
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        s = mfma32<E>(kop[kc], qa[kc], s);
-        ga[kc] = lds_row8<D, E>(g_l, 0, lane & 31, kc, gq);
+      for (int i = 0; i < NR; ++i) {
+        const int ks = i % KS;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          if (i < KS)
+            s[kh] = mfma16<E>(kop[kh][ks], op[i], s[kh]);
+          else
+            dp[kh] = mfma16<E>(vop[kh][ks], op[i], dp[kh]);
+        }
+        if (i + kLead < NR) rd(i + kLead);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) dp = mfma32<E>(vop[kc], ga[kc], dp);
-      const float lq = s_l[lane & 31];       // lse * log2(e) of this lane's query
-      const float dq = s_l[32 + (lane & 31)];  // D of this lane's query
+      const float lq = s_l[r];       // lse * log2(e) of this lane's query
+      const float dq = s_l[32 + r];  // D of this lane's query
       with_mask(!full, [&](auto masked) {
         // keys visible to this lane's query (none past the last row)
-        const int qi = i0 + (lane & 31);
+        const int qi = i0 + r;
         const int rlo = qi < a.nq ? mg.row_lo(qi) : 0, rhi = qi < a.nq ? mg.row_hi(qi) : 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float arg = fmaf(s[e], sl2, -lq);
-          if constexpr (decltype(masked)::value) {
-            const int kj = wk0 + 8 * (e >> 2) + 4 * gq + (e & 3);
-            arg = ((kj >= rlo) & (kj < rhi)) ? arg : -INFINITY;
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float arg = fmaf(s[kh][e], sl2, -lq);
+            if constexpr (decltype(masked)::value) {
+              const int kj = wk0 + 16 * kh + 4 * g4 + e;
+              arg = ((kj >= rlo) & (kj < rhi)) ? arg : -INFINITY;
+            }
+            s[kh][e] = fast_exp2(arg);
           }
-          s[e] = fast_exp2(arg);
-        }
       });
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dp[e] = s[e] * (dp[e] - dq);
-      // P^T and dS^T as [query][key] 32 x 32 tiles (ds_tile_off); the
-      // accumulate waves read them transposed
-      uint16_t* pt = p_l + kb * 1024;
-      uint16_t* dt = d_l + kb * 1024;
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const V8 pv = acc_chunk<E>(s, c);
-        const V8 v = acc_chunk<E>(dp, c);
-        *reinterpret_cast<V4*>(pt + ds_tile_off(lane & 31, 4 * c + gq)) = V4{pv[0], pv[1], pv[2], pv[3]};
-        *reinterpret_cast<V4*>(pt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) = V4{pv[4], pv[5], pv[6], pv[7]};
-        *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + gq)) = V4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<V4*>(dt + ds_tile_off(lane & 31, 4 * c + 2 + gq)) = V4{v[4], v[5], v[6], v[7]};
-      }
-      if (a.ds) {
-        // the block kept for the dQ pass: block i0 / 32 - wlo / 32 of this
-        // key block's ds_count() (in range because sees(j) holds)
-        kept = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems;
-        kv[0] = acc_chunk<E>(dp, 0);
-        kv[1] = acc_chunk<E>(dp, 1);
-      }
-    };
-    // End of a step: wait for the rows fetched at its start, then store the
-    // kept dS block straight from the registers, streamed past the caches
-    // like the output tiles.  The wait sits on every path, ahead of the
-    // stores, so the next step's put finds the staged rows retired instead
-    // of waiting for these stores as well.
-    auto keep = [&]() {
-      wait_vmem();
-      if (kept) {
+        for (int e = 0; e < 4; ++e) dp[kh][e] = s[kh][e] * (dp[kh][e] - dq);
+      // this lane's row of the [query][key] P and dS tiles of the key block
+      // (ds_tile_off, 4-key chunk 4 kh + g4); the accumulate waves read them
+      // transposed
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, kv[c]),
-                                      reinterpret_cast<u32x4*>(kept + (c * 64 + lane) * 8));
+      for (int kh = 0; kh < 2; ++kh) {
+        *reinterpret_cast<V4*>(p_l + woff[kh]) = __builtin_convertvector(s[kh], V4);
+        *reinterpret_cast<V4*>(d_l + woff[kh]) = __builtin_convertvector(dp[kh], V4);
       }
     };
 
     if (ntiles > 0) {
       __syncthreads();
       produce(sQ0, sG0, sS0, sP0, sD0, 0);
-      keep();
       __syncthreads();
     }
     // step j: load tile j + 2, produce tile j + 1 (the accumulate waves
-    // consume tile j meanwhile), keep its dS, barrier
+    // consume tile j meanwhile), barrier
     for (int j = 0; j < ntiles; j += 3) {
       if (j + 2 < ntiles) load(sQ2, sG2, sS2, j + 2);
       produce(sQ1, sG1, sS1, sP1, sD1, j + 1);
-      keep();
       __syncthreads();
       if (j + 1 >= ntiles) break;
       if (j + 3 < ntiles) load(sQ0, sG0, sS0, j + 3);
       produce(sQ2, sG2, sS2, sP2, sD2, j + 2);
-      keep();
       __syncthreads();
       if (j + 2 >= ntiles) break;
       if (j + 4 < ntiles) load(sQ1, sG1, sS1, j + 4);
       produce(sQ0, sG0, sS0, sP0, sD0, j + 3);
-      keep();
       __syncthreads();
     }
     // staging barriers of the accumulate waves' epilogue
@@ -648,9 +652,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
     __syncthreads();
   } else {
     // ----------------------------------------------------- accumulate waves
-    f32x16 dkacc[DB], dvacc[DB];
+    const int dh = wave & 1;  // head-dim half: dims 64 dh .. + 63
+    int trlo, trhi;           // lane offsets of the transposed reads, at dim 64 dh
+    tr_lane_offsets<D>(lane, trlo, trhi);
+    trlo += 64 * dh;
+    trhi += 64 * dh;
+    int dso[2][2];            // lane offsets of the P / dS tile reads
+    ds_tr_lane_offsets(lane, dso);
+    // kept dS blocks of this key block: the (b, h) base plus the blocks of
+    // the key blocks before it
+    uint16_t* dsb = a.ds;
+    int64_t ds0 = 0;
+    if (a.ds) {
+      dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
+      ds0 = ds_offset(mg, wk0 / 32, lane);
+    }
+    f32x16 dkacc[2], dvacc[2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < 2; ++db) {
       dkacc[db] = f32x16{};
       dvacc[db] = f32x16{};
     }
@@ -661,27 +680,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       // transposed reads of the [query][key] tiles
       const uint16_t* pt = p_l + kb * 1024;
       const uint16_t* dt = d_l + kb * 1024;
-      // operand reads run kLead products ahead of the product that uses them
-      // (the order is pinned by scheduling fences): product i of the 2 DB
-      // products per 16-row chunk c is dV (even i) or dK (odd i) of block
-      // db = (i / 2) % DB
-      constexpr int NP = 4 * DB, kLead = 8;
+      if (a.ds) {
+        // keep chunk dh of the dS block for the dQ pass: block
+        // i0 / 32 - wlo / 32 of this key block's ds_count() (in range because
+        // sees(j) holds), in that pass's operand order (lane l: query l % 32,
+        // keys 16 dh + 4 (l / 32) + 0..3 and 16 dh + 8 + 4 (l / 32) + 0..3),
+        // streamed past the caches like the output tiles
+        const int i0 = t0 + j * BQ;
+        const V4 x0 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + gq));
+        const V4 x1 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + 2 + gq));
+        uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems + (dh * 64 + lane) * 8;
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, V8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}),
+                                    reinterpret_cast<u32x4*>(blk));
+      }
+      // product i: 16-row chunk c = i / 4, block db = (i / 2) % 2 of this
+      // wave's dims, dV (even i) or dK (odd i); operand reads run kLead
+      // products ahead
+      constexpr int NP = 8, kLead = 4;
       V8 pop[2], dsop[2], op[NP];
       auto opread = [&](int i) {
-        const int c = i / (2 * DB), db = (i / 2) % DB;
-        op[i] = lds_tr8<D, E>((i & 1) ? q_l : g_l, 16 * c, 32 * db, lane);
+        const int c = i / 4, db = (i / 2) % 2;
+        op[i] = lds_tr8_at<E>((i & 1) ? q_l : g_l, trlo, trhi, 16 * c * tstride<D>() + 32 * db);
       };
+      // the lane offsets are re-read each step (opaque to loop-invariant
+      // hoisting, which would keep one address register per read and spill)
+      asm volatile("" : "+v"(trlo), "+v"(trhi), "+v"(dso[0][0]), "+v"(dso[0][1]), "+v"(dso[1][0]),
+                   "+v"(dso[1][1]));
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        pop[c] = lds_tr8_ds<E>(pt, 16 * c, 0, lane);
-        dsop[c] = lds_tr8_ds<E>(dt, 16 * c, 0, lane);
+        pop[c] = lds_tr8_ds_at<E>(pt, dso[c]);
+        dsop[c] = lds_tr8_ds_at<E>(dt, dso[c]);
       }
 #pragma unroll
       for (int i = 0; i < kLead; ++i) opread(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int c = i / (2 * DB), db = (i / 2) % DB;
+        const int c = i / 4, db = (i / 2) % 2;
         if (i & 1)
           dkacc[db] = mfma32<E>(op[i], dsop[c], dkacc[db]);
         else
@@ -695,35 +730,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       __syncthreads();
     }
     for (int j = 0; j < ntiles; j += 3) {
-      if (j + 2 < ntiles) load(sQ2, sG2, sS2, j + 2);
       consume(sQ0, sG0, sP0, sD0, j);
       __syncthreads();
       if (j + 1 >= ntiles) break;
-      if (j + 3 < ntiles) load(sQ0, sG0, sS0, j + 3);
       consume(sQ1, sG1, sP1, sD1, j + 1);
       __syncthreads();
       if (j + 2 >= ntiles) break;
-      if (j + 4 < ntiles) load(sQ1, sG1, sS1, j + 4);
       consume(sQ2, sG2, sP2, sD2, j + 2);
       __syncthreads();
     }
-    // dK, then dV: 32 rows per wave through sQ0 / sG0 / sQ1 / sG1
+    // dK, then dV: key block kb's 32 rows through sQ0 / sG0 / sQ1 / sG1,
+    // each wave its 64 dims
     uint16_t* mine = kb == 0 ? sQ0 : kb == 1 ? sG0 : kb == 2 ? sQ1 : sG1;
-    acc_to_lds<D, E>(mine, lane & 31, dkacc, a.scale, gq);
+    const int at = tid - NS;
+    acc_to_lds_cols<D, E, 2>(mine, lane & 31, dkacc, 64 * dh, a.scale, gq);
     __syncthreads();
     uint16_t* dK = (uint16_t*)a.dk + rslice<SR, D>(a.rdk, bh, a.H, a.nk);
-    store_tile<32, D, 256, SR>(dK, a.rdk, k0, a.nk, sQ0, tid - 256);
-    store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 32, a.nk, sG0, tid - 256);
-    store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 64, a.nk, sQ1, tid - 256);
-    store_tile<32, D, 256, SR>(dK, a.rdk, k0 + 96, a.nk, sG1, tid - 256);
+    store_tile<32, D, NS, SR>(dK, a.rdk, k0, a.nk, sQ0, at);
+    store_tile<32, D, NS, SR>(dK, a.rdk, k0 + 32, a.nk, sG0, at);
+    store_tile<32, D, NS, SR>(dK, a.rdk, k0 + 64, a.nk, sQ1, at);
+    store_tile<32, D, NS, SR>(dK, a.rdk, k0 + 96, a.nk, sG1, at);
     __syncthreads();
-    acc_to_lds<D, E>(mine, lane & 31, dvacc, 1.f, gq);
+    acc_to_lds_cols<D, E, 2>(mine, lane & 31, dvacc, 64 * dh, 1.f, gq);
     __syncthreads();
     uint16_t* dV = (uint16_t*)a.dv + rslice<SR, D>(a.rdv, bh, a.H, a.nk);
-    store_tile<32, D, 256, SR>(dV, a.rdv, k0, a.nk, sQ0, tid - 256);
-    store_tile<32, D, 256, SR>(dV, a.rdv, k0 + 32, a.nk, sG0, tid - 256);
-    store_tile<32, D, 256, SR>(dV, a.rdv, k0 + 64, a.nk, sQ1, tid - 256);
-    store_tile<32, D, 256, SR>(dV, a.rdv, k0 + 96, a.nk, sG1, tid - 256);
+    store_tile<32, D, NS, SR>(dV, a.rdv, k0, a.nk, sQ0, at);
+    store_tile<32, D, NS, SR>(dV, a.rdv, k0 + 32, a.nk, sG0, at);
+    store_tile<32, D, NS, SR>(dV, a.rdv, k0 + 64, a.nk, sQ1, at);
+    store_tile<32, D, NS, SR>(dV, a.rdv, k0 + 96, a.nk, sG1, at);
   }
 }
 
@@ -964,8 +998,8 @@ int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
   if (passes & kPassDKDV) {
     if constexpr (D == 128) {
       const int nkt = (a.nk + 127) / 128;
-      hipLaunchKernelGGL((dkdv_pp_kernel<E, D, kAnyMask, SR>),
-                         dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(512), 0, s, a, nkt);
+      hipLaunchKernelGGL((dkdv_k16_kernel<E, D, kAnyMask, SR>),
+                         dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(1024), 0, s, a, nkt);
     } else {
       constexpr int BK = 32 * DkdvShape<D>::KB * NW;
       const int nkt = (a.nk + BK - 1) / BK;

@@ -89,6 +89,27 @@ __device__ __forceinline__ typename E::v8 lds_tr8(const uint16_t* tile, int r0, 
   return __builtin_bit_cast(typename E::v8, w);
 }
 
+// lds_tr8 split into a per-lane part and a compile-time part: with
+// tr_lane_offsets(lane, lo, hi), lds_tr8(tile, r0, c0, lane) reads the same
+// elements as lds_tr8_at(tile, lo + x, hi + x, r0 * tstride + c0) for any
+// column shift x added to both (a multiple of 32).  One pair of lane
+// registers then addresses every read of a loop, the rest being immediates.
+template <int D>
+__device__ __forceinline__ void tr_lane_offsets(int lane, int& lo, int& hi) {
+  const int grp = lane >> 4, li = lane & 15;
+  const int rl = 4 * (grp >> 1) + (li >> 2), cl = 16 * (grp & 1) + 4 * (li & 3);
+  lo = toff2<D>(0, rl, 0, cl);
+  hi = toff2<D>(0, rl + 8, 0, cl);
+}
+template <typename E>
+__device__ __forceinline__ typename E::v8 lds_tr8_at(const uint16_t* tile, int lo, int hi, int imm) {
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + imm + lo));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + imm + hi));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 w = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(typename E::v8, w);
+}
+
 // Direct global -> LDS load of a ROWS x D bf16 tile (rows r0 .. r0+ROWS-1 of
 // the n rows of a slice, addressed through `rm` from the slice base `src`)
 // into the tile layout, by NT threads.  gfx950's
@@ -128,14 +149,17 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, con
   }
 }
 
-// The 32 x 32 dS staging tile of the dK/dV pass: row stride 32 elements,
-// 8-byte chunk k of row r stored at chunk position k ^ ((r / 4) % 8).  A
-// column of 8-byte pieces (32 rows, one chunk) then covers all 64 banks, and
-// the transposed reads (4 consecutive rows x 4 chunks per 16 lanes) stay
-// conflict-free; with a plain 64-byte stride the column accesses were 8-way
-// conflicts (measured with SQ_LDS_BANK_CONFLICT).  Element offset of
-// (row r, chunk k).
-__device__ __forceinline__ int ds_tile_off(int r, int k) { return r * 32 + 4 * (k ^ ((r >> 2) & 7)); }
+// The 32 x 32 P / dS staging tile of the backward: row stride 32 elements,
+// 8-byte chunk k of row r stored at chunk position k ^ f(r), f(r) =
+// 2 ((r / 4) % 4) + (r / 16) % 2.  A column of 8-byte pieces (32 rows, one
+// chunk) then covers all 64 banks, so do 16 rows x 2 adjacent chunks (the
+// writes from a 16 x 16 accumulator), and the transposed reads (4
+// consecutive rows x 4 chunks per 16 lanes) stay conflict-free; with a plain
+// 64-byte stride the column accesses were 8-way conflicts (measured with
+// SQ_LDS_BANK_CONFLICT).  Element offset of (row r, chunk k).
+__device__ __forceinline__ int ds_tile_off(int r, int k) {
+  return r * 32 + 4 * (k ^ ((((r >> 2) & 3) << 1) | ((r >> 4) & 1)));
+}
 
 // Transposed operand read of the dS staging tile, as lds_tr8: free index =
 // column c0 + lane % 32, contraction slots = rows r0 + 4g + e, r0 + 8 + 4g + e.
@@ -147,6 +171,28 @@ __device__ __forceinline__ typename E::v8 lds_tr8_ds(const uint16_t* tile, int r
   const int row = r0 + 4 * g + e, k = (c0 >> 2) + 4 * half + r;
   i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + ds_tile_off(row, k)));
   i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + ds_tile_off(row + 8, k)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename E::v8, w);
+}
+
+// Lane offsets of lds_tr8_ds(tile, 16 c, 0, lane), c = 0, 1: the two reads
+// at tile + o[c][0] and tile + o[c][1] (see lds_tr8_ds_at).
+__device__ __forceinline__ void ds_tr_lane_offsets(int lane, int (&o)[2][2]) {
+  const int grp = lane >> 4, li = lane & 15;
+  const int e = li >> 2, r = li & 3;
+  const int g = grp >> 1, half = grp & 1;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = 16 * c + 4 * g + e, k = 4 * half + r;
+    o[c][0] = ds_tile_off(row, k);
+    o[c][1] = ds_tile_off(row + 8, k);
+  }
+}
+template <typename E>
+__device__ __forceinline__ typename E::v8 lds_tr8_ds_at(const uint16_t* tile, const int (&o)[2]) {
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o[0]));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o[1]));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(typename E::v8, w);
@@ -242,6 +288,20 @@ __device__ __forceinline__ void acc_to_lds(uint16_t* tile, int row, const f32x16
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint2*>(tile + toff2<D>(0, row, 32 * db, 8 * i + 4 * gq)) =
+          pack4<E>(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul, acc[db][4 * i + 2] * mul,
+                   acc[db][4 * i + 3] * mul);
+}
+
+// acc_to_lds for NB of the D / 32 column blocks, starting at column c0 (a
+// multiple of 32): element (row, c0 + 32*db + 8*i + 4*gq + j) from acc[db].
+template <int D, typename E, int NB>
+__device__ __forceinline__ void acc_to_lds_cols(uint16_t* tile, int row, const f32x16 (&acc)[NB],
+                                                int c0, float mul, int gq) {
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint2*>(tile + toff2<D>(0, row, c0 + 32 * db, 8 * i + 4 * gq)) =
           pack4<E>(acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul, acc[db][4 * i + 2] * mul,
                    acc[db][4 * i + 3] * mul);
 }

@@ -7,6 +7,10 @@
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) + s, s = 0..7
 //   B (16 x 32): lane l holds col l%32, k = 8*(l/32) + s
 //   C (32 x 32): lane l holds col l%32, rows 8*i + 4*(l/32) + j in acc[4*i + j]
+// v_mfma_f32_16x16x32_bf16 / _f16 (checked on gfx950 hardware):
+//   A (16 x 32): lane l holds row l%16, k = 8*(l/16) + s
+//   B (32 x 16): lane l holds col l%16, k = 8*(l/16) + s
+//   C (16 x 16): lane l holds col l%16, rows 4*(l/16) + j in acc[j]
 // The contraction index k may be permuted freely as long as A and B agree;
 // the kernels use that to feed an accumulator straight back in as an operand.
 //
@@ -46,6 +50,9 @@ struct Bf16 {
   static __device__ __forceinline__ f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(const v8& a, const v8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
 };
 
 struct F16 {
@@ -55,12 +62,20 @@ struct F16 {
   static __device__ __forceinline__ f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(const v8& a, const v8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
 };
 
 template <typename E>
 __device__ __forceinline__ f32x16 mfma32(const typename E::v8& a, const typename E::v8& b,
                                          const f32x16& c) {
   return E::mfma(a, b, c);
+}
+template <typename E>
+__device__ __forceinline__ f32x4 mfma16(const typename E::v8& a, const typename E::v8& b,
+                                        const f32x4& c) {
+  return E::mfma16(a, b, c);
 }
 
 // Accumulator entries 8c .. 8c+7 of a 32x32 tile, rounded to E: the rows
@@ -82,14 +97,6 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// s_waitcnt vmcnt(0): wait until every vector memory load and store of the
-// wave has retired (export and LDS counters untouched).  On gfx950 loads and
-// stores share that one counter, so where a register-staged load is followed
-// by stores on some paths only, the compiler's own wait at the load's use has
-// to assume the stores and waits for them too; waiting here, before the
-// stores, leaves nothing outstanding on the staged registers.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // x on lane l combined with x on lane l ^ 32 (the same row's other half in
 // the MFMA accumulator layout).  v_permlane32_swap of x with itself leaves
