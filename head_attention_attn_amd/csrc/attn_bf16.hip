@@ -680,19 +680,6 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void 
       // transposed reads of the [query][key] tiles
       const uint16_t* pt = p_l + kb * 1024;
       const uint16_t* dt = d_l + kb * 1024;
-      if (a.ds) {
-        // keep chunk dh of the dS block for the dQ pass: block
-        // i0 / 32 - wlo / 32 of this key block's ds_count() (in range because
-        // sees(j) holds), in that pass's operand order (lane l: query l % 32,
-        // keys 16 dh + 4 (l / 32) + 0..3 and 16 dh + 8 + 4 (l / 32) + 0..3),
-        // streamed past the caches like the output tiles
-        const int i0 = t0 + j * BQ;
-        const V4 x0 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + gq));
-        const V4 x1 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + 2 + gq));
-        uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems + (dh * 64 + lane) * 8;
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, V8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}),
-                                    reinterpret_cast<u32x4*>(blk));
-      }
       // product i: 16-row chunk c = i / 4, block db = (i / 2) % 2 of this
       // wave's dims, dV (even i) or dK (odd i); operand reads run kLead
       // products ahead
@@ -723,6 +710,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void 
           dvacc[db] = mfma32<E>(op[i], pop[c], dvacc[db]);
         if (i + kLead < NP) opread(i + kLead);
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (a.ds) {
+        // keep chunk dh of the dS block for the dQ pass: block
+        // i0 / 32 - wlo / 32 of this key block's ds_count() (in range because
+        // sees(j) holds), in that pass's operand order (lane l: query l % 32,
+        // keys 16 dh + 4 (l / 32) + 0..3 and 16 dh + 8 + 4 (l / 32) + 0..3),
+        // streamed past the caches like the output tiles
+        const int i0 = t0 + j * BQ;
+        const V4 x0 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + gq));
+        const V4 x1 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + 2 + gq));
+        uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems + (dh * 64 + lane) * 8;
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, V8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}),
+                                    reinterpret_cast<u32x4*>(blk));
       }
     };
     if (ntiles > 0) {
