@@ -420,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   }
 }
 
-// dK/dV pass at D = 128: a workgroup of 16 waves (four per SIMD) for 128
+// dK/dV pass at D = 128: a workgroup of 12 waves (three per SIMD) for 128
 // keys, in two roles working one query tile apart.
 //   score waves 0..7: the two waves of key block kb = w / 2 hold its 32 K and
 //     V rows as register operands, and wave w takes query rows 16 (w % 2) ..
@@ -429,22 +429,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
 //     query 16 (w % 2) + l % 16, keys 4 (l / 16) .. + 3 of each 16-key
 //     half), P = exp(S*scale - lse) and dS = P (dP - D), rounded to E and
 //     handed over as its rows of the key block's [query][key] P and dS tiles
-//     (8-byte chunks swizzled by ds_tile_off); the score waves also load the
-//     Q / dO tiles and the row statistics;
-//   accumulate waves 8..15: wave 8 + m owns key block m / 2 and head-dim half
-//     m % 2: dV^T += dO^T P, dK^T += Q^T dS with 32x32x16 products, dO^T, Q^T
-//     and the P, dS operands from transpose reads; when the caller gave room,
-//     wave m % 2 of a key block also writes 16-key chunk m % 2 of each dS
-//     block to the workspace, in the dQ pass's operand order.
+//     (8-byte chunks swizzled by ds_tile_off), zeros where the key block
+//     sees none of the tile; the score waves also load the Q / dO tiles and
+//     the row statistics;
+//   accumulate waves 8..11: wave 8 + m owns key blocks 2 (m / 2) and
+//     2 (m / 2) + 1 (64 keys) and head-dim half m % 2: dV^T += dO^T P,
+//     dK^T += Q^T dS with 32x32x16 products, dO^T, Q^T and the P, dS
+//     operands from transpose reads, each dO^T / Q^T read feeding the
+//     products of both key blocks; when the caller gave room, wave m also
+//     writes 16-key chunk m % 2 of each visible dS block of its two key
+//     blocks to the workspace, in the dQ pass's operand order.
 // Splitting a key block's softmax arithmetic over two score waves halves the
 // dependency chain each carries per step (one wave per key block carried the
 // whole 32 x 32 tile before: 849 -> 781 us on the causal workload), with the
 // same LDS operand traffic: a score wave reads only its 16 query rows, each
-// read feeding the products of both key halves.  Q / dO tiles cycle through
+// read feeding the products of both key halves.  An accumulate wave over 64
+// keys rather than 32 reads each step's dO^T / Q^T operands once for two key
+// blocks: the accumulate waves' LDS reads per step fall from 104 to 72 KB
+// (790 -> 777 us causal, 441 -> 433 us sliding window; its 128 accumulator
+// registers set the three-waves-per-SIMD budget).  Q / dO tiles cycle through
 // three named buffers (one being loaded, one read by the score waves, one by
 // the accumulate waves), P / dS through three more.
 template <typename E, int D, int MODE, bool SR>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void dkdv_k16_kernel(BwdArgs a, int nkt) {
+__global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3))) void dkdv_k16_kernel(BwdArgs a, int nkt) {
   using V8 = typename E::v8;
   using V4 = typename E::v4;
   static_assert(D == 128, "16-key score waves: d = 128");
@@ -564,8 +571,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void 
 
     auto produce = [&](const uint16_t* q_l, const uint16_t* g_l, const float* s_l,
                        uint16_t* p_l, uint16_t* d_l, int j) {
-      if (!sees(j)) return;
       opaque();
+      if (!sees(j)) {
+        // zeros: the accumulate wave of this key block's pair multiplies
+        // both blocks' tiles whenever either block sees the tile
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          *reinterpret_cast<V4*>(p_l + woff[kh]) = V4{};
+          *reinterpret_cast<V4*>(d_l + woff[kh]) = V4{};
+        }
+        return;
+      }
       const int i0 = t0 + j * BQ;
       const bool full = wk1 == wk0 + 32 && mg.tile_full(i0 + 16 * qh, i0 + 16 * qh + 16, wk0, wk1);
       // read i: the B operand (32 dims x 16 queries) of head-dim chunk
@@ -652,77 +668,103 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void 
     __syncthreads();
   } else {
     // ----------------------------------------------------- accumulate waves
-    const int dh = wave & 1;  // head-dim half: dims 64 dh .. + 63
+    // wave 8 + w: key blocks 2 kp and 2 kp + 1 (kp = w / 2, 64 keys), head
+    // dims 64 dh .. + 63 (dh = w % 2)
+    const int kp = (wave - 8) >> 1, dh = wave & 1;
     int trlo, trhi;           // lane offsets of the transposed reads, at dim 64 dh
     tr_lane_offsets<D>(lane, trlo, trhi);
     trlo += 64 * dh;
     trhi += 64 * dh;
     int dso[2][2];            // lane offsets of the P / dS tile reads
     ds_tr_lane_offsets(lane, dso);
-    // kept dS blocks of this key block: the (b, h) base plus the blocks of
-    // the key blocks before it
+    // query range and first kept dS block of each of the two key blocks
+    int blo[2] = {0, 0}, bhi[2] = {0, 0};
+    int64_t bds[2] = {0, 0};
     uint16_t* dsb = a.ds;
-    int64_t ds0 = 0;
-    if (a.ds) {
-      dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
-      ds0 = ds_offset(mg, wk0 / 32, lane);
-    }
-    f32x16 dkacc[2], dvacc[2];
+    if (a.ds) dsb += (int64_t)bh * a.ds_per_bh * kDsBlockElems;
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      dkacc[db] = f32x16{};
-      dvacc[db] = f32x16{};
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const int bk0 = k0 + 32 * (2 * kp + b2);
+      if (bk0 < a.nk) mg.query_range(bk0, min(bk0 + 32, a.nk), &blo[b2], &bhi[b2]);
+      if (a.ds) {
+        // every lane holds the total: keep it in scalar registers
+        const int64_t v = ds_offset(mg, bk0 / 32, lane);
+        const uint32_t vlo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t vhi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        bds[b2] = (int64_t)(((uint64_t)vhi << 32) | vlo) - blo[b2] / 32;
+      }
     }
+    // kept-dS copy: this lane's two 8-byte reads of a dS tile and its 16
+    // bytes of a block
+    int cpo[2] = {ds_tile_off(lane & 31, 4 * dh + gq), ds_tile_off(lane & 31, 4 * dh + 2 + gq)};
+    const int cpl = (dh * 64 + lane) * 8;
+    auto seesb = [&](int j, int b2) {
+      const int i0 = t0 + j * BQ;
+      return blo[b2] < bhi[b2] && i0 < bhi[b2] && i0 + BQ > blo[b2];
+    };
+    f32x16 dkacc[2][2], dvacc[2][2];  // [key block][32-dim block]
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        dkacc[b2][db] = f32x16{};
+        dvacc[b2][db] = f32x16{};
+      }
     auto consume = [&](const uint16_t* q_l, const uint16_t* g_l, const uint16_t* p_l,
                        const uint16_t* d_l, int j) {
-      if (!sees(j)) return;
-      // P and dS operands (lane = key, 8 queries of a 16-row chunk) by
-      // transposed reads of the [query][key] tiles
-      const uint16_t* pt = p_l + kb * 1024;
-      const uint16_t* dt = d_l + kb * 1024;
-      // product i: 16-row chunk c = i / 4, block db = (i / 2) % 2 of this
-      // wave's dims, dV (even i) or dK (odd i); operand reads run kLead
-      // products ahead
-      constexpr int NP = 8, kLead = 4;
-      V8 pop[2], dsop[2], op[NP];
-      auto opread = [&](int i) {
-        const int c = i / 4, db = (i / 2) % 2;
-        op[i] = lds_tr8_at<E>((i & 1) ? q_l : g_l, trlo, trhi, 16 * c * tstride<D>() + 32 * db);
-      };
-      // the lane offsets are re-read each step (opaque to loop-invariant
-      // hoisting, which would keep one address register per read and spill)
+      if (!seesb(j, 0) && !seesb(j, 1)) return;
+      const uint16_t* pt = p_l + 2 * kp * 1024;
+      const uint16_t* dt = d_l + 2 * kp * 1024;
       asm volatile("" : "+v"(trlo), "+v"(trhi), "+v"(dso[0][0]), "+v"(dso[0][1]), "+v"(dso[1][0]),
-                   "+v"(dso[1][1]));
+                   "+v"(dso[1][1]), "+v"(cpo[0]), "+v"(cpo[1]));
+      // phase f = 2 c + kind: 16-row chunk c, dV (kind 0: dO^T x P) or dK
+      // (kind 1: Q^T x dS); operands X[db] (dims 32 db of this wave's half)
+      // and Y[b2] (key block 2 kp + b2); each X read feeds two products.
+      // Read r of the 16: phase r / 4, X0 X1 Y0 Y1; issued one phase ahead
+      constexpr int NR = 16;
+      V8 rd[NR];
+      auto issue = [&](int r) {
+        const int f = r / 4, c = f / 2, kind = f % 2, q = r % 4;
+        if (q < 2)
+          rd[r] = lds_tr8_at<E>(kind ? q_l : g_l, trlo, trhi, 16 * c * tstride<D>() + 32 * q);
+        else
+          rd[r] = lds_tr8_ds_at<E>((kind ? dt : pt) + (q - 2) * 1024, dso[c]);
+      };
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        pop[c] = lds_tr8_ds_at<E>(pt, dso[c]);
-        dsop[c] = lds_tr8_ds_at<E>(dt, dso[c]);
-      }
-#pragma unroll
-      for (int i = 0; i < kLead; ++i) opread(i);
+      for (int r = 0; r < 4; ++r) issue(r);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        const int c = i / 4, db = (i / 2) % 2;
-        if (i & 1)
-          dkacc[db] = mfma32<E>(op[i], dsop[c], dkacc[db]);
-        else
-          dvacc[db] = mfma32<E>(op[i], pop[c], dvacc[db]);
-        if (i + kLead < NP) opread(i + kLead);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int f = 0; f < 4; ++f) {
+        const int kind = f % 2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int db = k / 2, b2 = k % 2;
+          const V8 x = rd[4 * f + db], y = rd[4 * f + 2 + b2];
+          if (kind)
+            dkacc[b2][db] = mfma32<E>(x, y, dkacc[b2][db]);
+          else
+            dvacc[b2][db] = mfma32<E>(x, y, dvacc[b2][db]);
+          if (f < 3) issue(4 * (f + 1) + k);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       if (a.ds) {
-        // keep chunk dh of the dS block for the dQ pass: block
-        // i0 / 32 - wlo / 32 of this key block's ds_count() (in range because
-        // sees(j) holds), in that pass's operand order (lane l: query l % 32,
-        // keys 16 dh + 4 (l / 32) + 0..3 and 16 dh + 8 + 4 (l / 32) + 0..3),
-        // streamed past the caches like the output tiles
+        // keep chunk dh of each visible dS block for the dQ pass (block
+        // i0 / 32 - blo / 32 of that key block's ds_count(); bds holds the
+        // first block's index less blo / 32), in that pass's
+        // operand order, streamed past the caches like the output tiles
         const int i0 = t0 + j * BQ;
-        const V4 x0 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + gq));
-        const V4 x1 = *reinterpret_cast<const V4*>(dt + ds_tile_off(lane & 31, 4 * dh + 2 + gq));
-        uint16_t* blk = dsb + (ds0 + (int64_t)(i0 / 32 - wlo / 32)) * kDsBlockElems + (dh * 64 + lane) * 8;
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, V8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}),
-                                    reinterpret_cast<u32x4*>(blk));
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          if (!seesb(j, b2)) continue;
+          const uint16_t* t = dt + b2 * 1024;
+          const V4 x0 = *reinterpret_cast<const V4*>(t + cpo[0]);
+          const V4 x1 = *reinterpret_cast<const V4*>(t + cpo[1]);
+          uint16_t* blk = dsb + (bds[b2] + i0 / 32) * kDsBlockElems + cpl;
+          __builtin_nontemporal_store(
+              __builtin_bit_cast(u32x4, V8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}),
+              reinterpret_cast<u32x4*>(blk));
+        }
       }
     };
     if (ntiles > 0) {
@@ -739,25 +781,29 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) void 
       consume(sQ2, sG2, sP2, sD2, j + 2);
       __syncthreads();
     }
-    // dK, then dV: key block kb's 32 rows through sQ0 / sG0 / sQ1 / sG1,
-    // each wave its 64 dims
-    uint16_t* mine = kb == 0 ? sQ0 : kb == 1 ? sG0 : kb == 2 ? sQ1 : sG1;
+    // dK, then dV: key block kb's 32 rows through sQ0 / sG0 / sQ1 / sG1
+    // (kb = 0 .. 3), each wave its two blocks' 64 dims
+    uint16_t* m0 = kp == 0 ? sQ0 : sQ1;
+    uint16_t* m1 = kp == 0 ? sG0 : sG1;
+    constexpr int NA = 256;
     const int at = tid - NS;
-    acc_to_lds_cols<D, E, 2>(mine, lane & 31, dkacc, 64 * dh, a.scale, gq);
+    acc_to_lds_cols<D, E, 2>(m0, lane & 31, dkacc[0], 64 * dh, a.scale, gq);
+    acc_to_lds_cols<D, E, 2>(m1, lane & 31, dkacc[1], 64 * dh, a.scale, gq);
     __syncthreads();
     uint16_t* dK = (uint16_t*)a.dk + rslice<SR, D>(a.rdk, bh, a.H, a.nk);
-    store_tile<32, D, NS, SR>(dK, a.rdk, k0, a.nk, sQ0, at);
-    store_tile<32, D, NS, SR>(dK, a.rdk, k0 + 32, a.nk, sG0, at);
-    store_tile<32, D, NS, SR>(dK, a.rdk, k0 + 64, a.nk, sQ1, at);
-    store_tile<32, D, NS, SR>(dK, a.rdk, k0 + 96, a.nk, sG1, at);
+    store_tile<32, D, NA, SR>(dK, a.rdk, k0, a.nk, sQ0, at);
+    store_tile<32, D, NA, SR>(dK, a.rdk, k0 + 32, a.nk, sG0, at);
+    store_tile<32, D, NA, SR>(dK, a.rdk, k0 + 64, a.nk, sQ1, at);
+    store_tile<32, D, NA, SR>(dK, a.rdk, k0 + 96, a.nk, sG1, at);
     __syncthreads();
-    acc_to_lds_cols<D, E, 2>(mine, lane & 31, dvacc, 64 * dh, 1.f, gq);
+    acc_to_lds_cols<D, E, 2>(m0, lane & 31, dvacc[0], 64 * dh, 1.f, gq);
+    acc_to_lds_cols<D, E, 2>(m1, lane & 31, dvacc[1], 64 * dh, 1.f, gq);
     __syncthreads();
     uint16_t* dV = (uint16_t*)a.dv + rslice<SR, D>(a.rdv, bh, a.H, a.nk);
-    store_tile<32, D, NS, SR>(dV, a.rdv, k0, a.nk, sQ0, at);
-    store_tile<32, D, NS, SR>(dV, a.rdv, k0 + 32, a.nk, sG0, at);
-    store_tile<32, D, NS, SR>(dV, a.rdv, k0 + 64, a.nk, sQ1, at);
-    store_tile<32, D, NS, SR>(dV, a.rdv, k0 + 96, a.nk, sG1, at);
+    store_tile<32, D, NA, SR>(dV, a.rdv, k0, a.nk, sQ0, at);
+    store_tile<32, D, NA, SR>(dV, a.rdv, k0 + 32, a.nk, sG0, at);
+    store_tile<32, D, NA, SR>(dV, a.rdv, k0 + 64, a.nk, sQ1, at);
+    store_tile<32, D, NA, SR>(dV, a.rdv, k0 + 96, a.nk, sG1, at);
   }
 }
 
@@ -999,7 +1045,7 @@ int launch_bwd_dm(const BwdArgs& a, hipStream_t s, int passes) {
     if constexpr (D == 128) {
       const int nkt = (a.nk + 127) / 128;
       hipLaunchKernelGGL((dkdv_k16_kernel<E, D, kAnyMask, SR>),
-                         dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(1024), 0, s, a, nkt);
+                         dim3((unsigned)((int64_t)nkt * a.B * a.H)), dim3(768), 0, s, a, nkt);
     } else {
       constexpr int BK = 32 * DkdvShape<D>::KB * NW;
       const int nkt = (a.nk + BK - 1) / BK;
