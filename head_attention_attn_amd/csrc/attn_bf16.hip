@@ -40,7 +40,7 @@ namespace {
 constexpr float kSlack = 8.f;  // log2 of the largest unnormalised P
 
 template <typename E, int D, int NW, int MODE, bool SR, bool SB>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdArgs a, int nqt) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && D <= 96) ? 4 : 2))) void fwd_bf16_kernel(FwdArgs a, int nqt) {
   using V8 = typename E::v8;
   static_assert(NW == 4, "O staging assumes 4 waves (two 64-row tiles)");
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, TE = tile_elems<BN, D>();
@@ -50,7 +50,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // With few keys per row (SB: Nk <= 256, at most four tiles) one buffer:
   // half the LDS lets more workgroups share a CU, and they hide each
   // other's tile loads better than a workgroup's own prefetch does
-  // (measured on the N = 196 workload: 30 -> 26 us)
+  // (measured on the N = 196 workload: 30 -> 26 us).  There, at d <= 96,
+  // each tile is taken as two 32-key halves with an online-softmax update
+  // each: half the score registers, so four waves per SIMD fit and all of
+  // that workload's workgroups run at once (26.5 -> 23.7 us)
   __shared__ __attribute__((aligned(16))) uint16_t sK0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sV0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[SB ? 8 : TE];
@@ -163,6 +166,60 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
+  // the 32-key half mb of a staged tile, with its own online-softmax
+  // update: half the score registers of a whole tile
+  auto half_tile = [&](const uint16_t* k_l, const uint16_t* v_l, int j0, int mb) {
+    const int h0 = j0 + 32 * mb;
+    if (!(wlo < whi && h0 < whi && h0 + 32 > wlo)) return;
+    const bool full = mg.tile_full(wa, wb, h0, h0 + 32);
+    f32x16 sc = {};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      sc = mfma32<E>(lds_row8<D, E>(k_l, mb * 32, lane & 31, kc, gq), qop[kc], sc);
+    const float meff = m == -INFINITY ? 0.f : m;
+    float mx = -INFINITY;
+    with_mask(!full, [&](auto masked) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = fmaf(sc[e], sl2, -meff);
+        if constexpr (decltype(masked)::value) {
+          const int key = h0 + 8 * (e >> 2) + 4 * gq + (e & 3);
+          x = (key >= rlo) & (key < rhi) ? x : -INFINITY;
+        }
+        sc[e] = x;
+        mx = fmaxf(mx, x);
+      }
+    });
+    mx = max_halves(mx);
+    const bool need = m == -INFINITY ? mx > -INFINITY : mx > kSlack;
+    if (__any(need)) {
+      const float sh = need ? mx : 0.f;
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(-sh);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] -= sh;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      if (need) m = meff + sh;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = fast_exp2(sc[e]);
+      sc[e] = p;
+      rs += p;
+    }
+    rs = sum_halves(rs);
+    l += rs;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const V8 pop = acc_chunk<E>(sc, c2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = mfma32<E>(lds_tr8<D, E>(v_l, 16 * (2 * mb + c2), 32 * db, lane), pop, oacc[db]);
+    }
+  };
+
   if (SB && lo < hi) {
     for (int j0 = t0; j0 < hi; j0 += BN) {
       if (j0 != t0) {
@@ -170,7 +227,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         dma_tile<BN, D, NT, SR>(sV0, V, a.rv, j0, a.nk, tid);
       }
       __syncthreads();
-      tile(sK0, sV0, j0);
+      if constexpr (D <= 96) {
+        half_tile(sK0, sV0, j0, 0);
+        half_tile(sK0, sV0, j0, 1);
+      } else {
+        tile(sK0, sV0, j0);
+      }
       __syncthreads();
     }
   } else if (!SB && lo < hi) {
