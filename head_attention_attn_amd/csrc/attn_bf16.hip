@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
           float x = fmaf(s[mb][e], sl2, -meff);
           if constexpr (decltype(masked)::value) {
             const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * gq + (e & 3);
-            x = (key >= rlo) & (key < rhi) ? x : -INFINITY;
+            x = ((key >= rlo) & (key < rhi)) ? x : -INFINITY;
           }
           s[mb][e] = x;
           mx = fmaxf(mx, x);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
         float x = fmaf(sc[e], sl2, -meff);
         if constexpr (decltype(masked)::value) {
           const int key = h0 + 8 * (e >> 2) + 4 * gq + (e & 3);
-          x = (key >= rlo) & (key < rhi) ? x : -INFINITY;
+          x = ((key >= rlo) & (key < rhi)) ? x : -INFINITY;
         }
         sc[e] = x;
         mx = fmaxf(mx, x);
