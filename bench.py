@@ -547,14 +547,34 @@ class Step:
                    for i, kn in enumerate(self.kernels)}
         return ms_per_step, kern_ms, step_spread(ev, self.kernels)
 
-    def graph_time(self, replays: int) -> float:
+    def direct_time(self, steps: int) -> float:
+        """ms per step of ``steps`` direct steps between two events (no
+        per-kernel events): the reference that the autograd and graph timings,
+        taken later in the run, are compared with when timed next to it (the
+        MFMA-heavy kernels' clock drifts down over a run)."""
+        torch = self.torch
+        torch.cuda.synchronize(self.dev)
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for _ in range(steps):
+            self.run()
+        d1.record()
+        torch.cuda.synchronize(self.dev)
+        return d0.elapsed_time(d1) / steps
+
+    def graph_time(self, replays: int, warm: int = 20) -> float:
         """ms per step of the step captured once in a HIP graph and replayed
-        ``replays`` times: the kernels without the host's per-call work."""
+        ``replays`` times: the kernels without the host's per-call work.
+        ``warm`` untimed replays first: the capture leaves the GPU idle, and
+        the MFMA-heavy kernels run up to 25% slower for the first ~20 ms of
+        work after an idle spell (traced on the causal workload), as at the
+        start of the main region, whose warmup steps absorb it."""
         torch = self.torch
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             self.run()
-        graph.replay()
+        for _ in range(warm):
+            graph.replay()
         torch.cuda.synchronize(self.dev)
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
@@ -743,7 +763,8 @@ def main() -> int:
         + ", ".join(f"{kn} {kern_ms[kn]:.4f}" for kn in kernels))
 
     # the same step through the autograd wrapper (forward, then backward from
-    # dO by torch.autograd.grad), timed on its own after the main region
+    # dO by torch.autograd.grad), timed after the main region between two
+    # blocks of direct steps, its ratio taken against their mean
     autograd_rec = None
     if args.autograd_steps > 0:
         qa, ka, va = (t.detach().requires_grad_(True) for t in (st.q, st.k, st.v))
@@ -762,7 +783,7 @@ def main() -> int:
 
         for _ in range(3):
             ag_step()
-        torch.cuda.synchronize(dev)
+        before = st.direct_time(args.autograd_steps)
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record()
         for _ in range(args.autograd_steps):
@@ -770,19 +791,25 @@ def main() -> int:
         a1.record()
         torch.cuda.synchronize(dev)
         ag_ms = a0.elapsed_time(a1) / args.autograd_steps
+        adjacent = 0.5 * (before + st.direct_time(args.autograd_steps))
         autograd_rec = {"ms_per_step": round(ag_ms, 5), "steps": args.autograd_steps,
-                        "over_direct_calls": round(ag_ms / ms_per_step, 4)}
+                        "adjacent_direct_ms_per_step": round(adjacent, 5),
+                        "over_direct_calls": round(ag_ms / adjacent, 4)}
         log(f"[bench] autograd wrapper: {ag_ms:.4f} ms/step")
         del qa, ka, va
 
     # the same step captured once in a HIP graph and replayed: the kernels
     # without the host's per-call launch work (every call takes preallocated
-    # outputs and workspace, so the capture allocates nothing)
+    # outputs and workspace, so the capture allocates nothing); its ratio is
+    # taken against direct steps timed just before and after the replays
     graph_rec = None
     if args.graph_steps > 0:
+        before = st.direct_time(args.graph_steps)
         g_ms = st.graph_time(args.graph_steps)
+        adjacent = 0.5 * (before + st.direct_time(args.graph_steps))
         graph_rec = {"ms_per_step": round(g_ms, 5), "steps": args.graph_steps,
-                     "over_direct_calls": round(g_ms / ms_per_step, 4)}
+                     "adjacent_direct_ms_per_step": round(adjacent, 5),
+                     "over_direct_calls": round(g_ms / adjacent, 4)}
         log(f"[bench] HIP graph replay: {g_ms:.4f} ms/step")
 
     # cache-flushed steps: before each, a read of a buffer four times the
