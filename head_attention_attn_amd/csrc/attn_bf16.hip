@@ -777,6 +777,9 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3))) void d
       if (!seesb(j, 0) && !seesb(j, 1)) return;
       const uint16_t* pt = p_l + 2 * kp * 1024;
       const uint16_t* dt = d_l + 2 * kp * 1024;
+      // the lane offsets are re-read each step (opaque to loop-invariant
+      // hoisting, which would keep one address register per read and buffer
+      // set and spill)
       asm volatile("" : "+v"(trlo), "+v"(trhi), "+v"(dso[0][0]), "+v"(dso[0][1]), "+v"(dso[1][0]),
                    "+v"(dso[1][1]), "+v"(cpo[0]), "+v"(cpo[1]));
       // phase f = 2 c + kind: 16-row chunk c, dV (kind 0: dO^T x P) or dK
@@ -813,8 +816,10 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3))) void d
       if (a.ds) {
         // keep chunk dh of each visible dS block for the dQ pass (block
         // i0 / 32 - blo / 32 of that key block's ds_count(); bds holds the
-        // first block's index less blo / 32), in that pass's
-        // operand order, streamed past the caches like the output tiles
+        // first block's index less blo / 32), in that pass's operand order
+        // (lane l: query l % 32, keys 16 dh + 4 (l / 32) + 0..3 and
+        // 16 dh + 8 + 4 (l / 32) + 0..3), streamed past the caches like the
+        // output tiles
         const int i0 = t0 + j * BQ;
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
