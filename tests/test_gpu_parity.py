@@ -78,10 +78,13 @@ def test_fp32_ragged(d, mask, window):
     parity_case(1, 2, 77, 77, d, "fp32", mask, window, seed=2)
 
 
+@pytest.mark.parametrize("d", [64, 96])
 @pytest.mark.parametrize("n", [1, 17, 63, 64, 65, 129])
 @pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 8)])
-def test_bf16_lengths(n, mask, window):
-    parity_case(1, 3, n, n, 64, "bf16", mask, window, seed=n)
+def test_bf16_lengths(n, mask, window, d):
+    """Short sequences: one key tile taken as two 32-key halves (the second
+    one empty, partial or full), a partial second tile, and a single row."""
+    parity_case(1, 3, n, n, d, "bf16", mask, window, seed=n)
 
 
 @pytest.mark.parametrize("nq,nk,mask,window", [
