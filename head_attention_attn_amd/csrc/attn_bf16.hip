@@ -519,6 +519,11 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3))) void d
   static_assert(D == 128, "16-key score waves: d = 128");
   constexpr int NS = 512, BK = 128, BQ = 32, TE = tile_elems<BQ, D>();
   constexpr int KS = D / 32, PE = 4 * 2 * 64 * 8;  // 4 blocks x 2 chunks x 64 lanes x 16 B
+  // the staged Q / dO tiles are read by rows 16 at a time (the score waves'
+  // B operands) and transposed (the accumulate waves): the chunk swizzle on
+  // row bits 1, 2 keeps both conflict-free.  The epilogue reuses two of them
+  // as staging in the default layout.
+  constexpr int kQdSwz = 1;
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sG0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t sQ1[TE];
@@ -588,8 +593,8 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int g4 = lane >> 4;                // key group: keys 4 g4 .. + 3 of a 16-key half
     const int r = 16 * qh + (lane & 15);     // this lane's tile row
     static_assert(BQ * D / 8 == NS, "one 16-byte piece of a staged tile per thread");
-    int poff = toff<D>(tid / (D / 8), (tid % (D / 8)) * 8);
-    int roff = toff2<D>(16 * qh, lane & 15, 0, 8 * g4);
+    int poff = toff<D, kQdSwz>(tid / (D / 8), (tid % (D / 8)) * 8);
+    int roff = toff2<D, kQdSwz>(16 * qh, lane & 15, 0, 8 * g4);
     int woff[2] = {kb * 1024 + ds_tile_off(r, g4), kb * 1024 + ds_tile_off(r, 4 + g4)};
     int soff = tid;
     auto opaque = [&]() {
@@ -734,7 +739,7 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3))) void d
     // dims 64 dh .. + 63 (dh = w % 2)
     const int kp = (wave - 8) >> 1, dh = wave & 1;
     int trlo, trhi;           // lane offsets of the transposed reads, at dim 64 dh
-    tr_lane_offsets<D>(lane, trlo, trhi);
+    tr_lane_offsets<D, kQdSwz>(lane, trlo, trhi);
     trlo += 64 * dh;
     trhi += 64 * dh;
     int dso[2][2];            // lane offsets of the P / dS tile reads

@@ -38,10 +38,15 @@ __host__ __device__ constexpr int tstride() {
   return D == 128 ? 160 : 96;
 }
 
-// element offset of (row r, column col) in a tile; col % 4 == 0
-template <int D>
+// element offset of (row r, column col) in a tile; col % 4 == 0.  The
+// 16-byte chunks of a row are permuted in groups of four by bits SW, SW + 1
+// of the row: with SW = 2, 32 lanes reading rows 0..31 at one chunk are
+// conflict-free; with SW = 1, 16 lanes reading rows 0..15 at one chunk (and
+// the other 48 lanes the next chunks) are; the transposed reads are
+// conflict-free under either
+template <int D, int SW = 2>
 __device__ __forceinline__ int toff(int r, int col) {
-  return r * tstride<D>() + ((((col >> 3) ^ ((r >> 2) & 3)) << 3) | (col & 7));
+  return r * tstride<D>() + ((((col >> 3) ^ ((r >> SW) & 3)) << 3) | (col & 7));
 }
 
 // The same offset for row r0 + rl, column c0 + cl, written so that the part
@@ -49,9 +54,9 @@ __device__ __forceinline__ int toff(int r, int col) {
 // in the kernels' unrolled loops -- is a plain sum: the swizzle then depends
 // on the per-lane rl, cl only, and the compiler folds r0, c0 into the
 // instruction's immediate offset.  0 <= cl < 32.
-template <int D>
+template <int D, int SW = 2>
 __device__ __forceinline__ int toff2(int r0, int rl, int c0, int cl) {
-  return (r0 + rl) * tstride<D>() + c0 + (((((cl >> 3) & 3) ^ ((rl >> 2) & 3)) << 3) | (cl & 7));
+  return (r0 + rl) * tstride<D>() + c0 + (((((cl >> 3) & 3) ^ ((rl >> SW) & 3)) << 3) | (cl & 7));
 }
 
 // elements of a ROWS-row tile
@@ -94,12 +99,12 @@ __device__ __forceinline__ typename E::v8 lds_tr8(const uint16_t* tile, int r0, 
 // elements as lds_tr8_at(tile, lo + x, hi + x, r0 * tstride + c0) for any
 // column shift x added to both (a multiple of 32).  One pair of lane
 // registers then addresses every read of a loop, the rest being immediates.
-template <int D>
+template <int D, int SW = 2>
 __device__ __forceinline__ void tr_lane_offsets(int lane, int& lo, int& hi) {
   const int grp = lane >> 4, li = lane & 15;
   const int rl = 4 * (grp >> 1) + (li >> 2), cl = 16 * (grp & 1) + 4 * (li & 3);
-  lo = toff2<D>(0, rl, 0, cl);
-  hi = toff2<D>(0, rl + 8, 0, cl);
+  lo = toff2<D, SW>(0, rl, 0, cl);
+  hi = toff2<D, SW>(0, rl + 8, 0, cl);
 }
 template <typename E>
 __device__ __forceinline__ typename E::v8 lds_tr8_at(const uint16_t* tile, int lo, int hi, int imm) {
