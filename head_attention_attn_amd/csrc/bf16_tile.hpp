@@ -155,15 +155,16 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, con
 }
 
 // The 32 x 32 P / dS staging tile of the backward: row stride 32 elements,
-// 8-byte chunk k of row r stored at chunk position k ^ f(r), f(r) =
-// 2 ((r / 4) % 4) + (r / 16) % 2.  A column of 8-byte pieces (32 rows, one
-// chunk) then covers all 64 banks, so do 16 rows x 2 adjacent chunks (the
-// writes from a 16 x 16 accumulator), and the transposed reads (4
-// consecutive rows x 4 chunks per 16 lanes) stay conflict-free; with a plain
-// 64-byte stride the column accesses were 8-way conflicts (measured with
-// SQ_LDS_BANK_CONFLICT).  Element offset of (row r, chunk k).
+// 8-byte chunk k of row r stored at chunk position k ^ ((r / 2) % 8).  With
+// a plain 64-byte stride the column accesses (32 rows, one chunk) were 8-way
+// conflicts (SQ_LDS_BANK_CONFLICT).  Measured with an LDS microbenchmark:
+// 8-byte accesses of 32 rows at one chunk per 32 lanes, or of 16 rows x 2
+// adjacent chunks (the writes from a 16 x 16 accumulator), run at full rate
+// under this f and at half rate under f(r) = 2 ((r / 4) % 4) + (r / 16) % 2;
+// the transposed reads (4 consecutive rows x 4 chunks per 16 lanes) run at
+// the same rate under both.  Element offset of (row r, chunk k).
 __device__ __forceinline__ int ds_tile_off(int r, int k) {
-  return r * 32 + 4 * (k ^ ((((r >> 2) & 3) << 1) | ((r >> 4) & 1)));
+  return r * 32 + 4 * (k ^ ((r >> 1) & 7));
 }
 
 // Transposed operand read of the dS staging tile, as lds_tr8: free index =
