@@ -84,10 +84,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
   const int rhi = qvalid ? mg.row_hi(myq) : 0;
   const float sl2 = a.scale * kLog2e;
   const int t0 = range_tile_row(lo, BN, 0);
+  // K / V tile loads; the short-sequence half-tile path (128 registers)
+  // computes its lane offsets per load instead of holding them
+  DmaLanes<BN, D, NT> dl(tid);
+  auto dma = [&](uint16_t* t_l, const uint16_t* src, const RowMap& rm, int r0) {
+    if constexpr (SB && D <= 96)
+      dma_tile<BN, D, NT, SR>(t_l, src, rm, r0, a.nk, tid);
+    else
+      dma_tile_lanes<BN, D, NT, SR>(t_l, src, rm, r0, a.nk, tid, dl.off);
+  };
 
   if (lo < hi) {
-    dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
-    dma_tile<BN, D, NT, SR>(sV0, V, a.rv, t0, a.nk, tid);
+    dma(sK0, K, a.rk, t0);
+    dma(sV0, V, a.rv, t0);
   }
   V8 qop[KC];
   load_operand_rows<D, E>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
@@ -223,8 +232,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
   if (SB && lo < hi) {
     for (int j0 = t0; j0 < hi; j0 += BN) {
       if (j0 != t0) {
-        dma_tile<BN, D, NT, SR>(sK0, K, a.rk, j0, a.nk, tid);
-        dma_tile<BN, D, NT, SR>(sV0, V, a.rv, j0, a.nk, tid);
+        dma(sK0, K, a.rk, j0);
+        dma(sV0, V, a.rv, j0);
       }
       __syncthreads();
       if constexpr (D <= 96) {
@@ -239,15 +248,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
     __syncthreads();
     for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
       if (j0 + BN < hi) {
-        dma_tile<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid);
-        dma_tile<BN, D, NT, SR>(sV1, V, a.rv, j0 + BN, a.nk, tid);
+        dma(sK1, K, a.rk, j0 + BN);
+        dma(sV1, V, a.rv, j0 + BN);
       }
       tile(sK0, sV0, j0);
       __syncthreads();
       if (j0 + BN >= hi) break;
       if (j0 + 2 * BN < hi) {
-        dma_tile<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid);
-        dma_tile<BN, D, NT, SR>(sV0, V, a.rv, j0 + 2 * BN, a.nk, tid);
+        dma(sK0, K, a.rk, j0 + 2 * BN);
+        dma(sV0, V, a.rv, j0 + 2 * BN);
       }
       tile(sK1, sV1, j0 + BN);
       __syncthreads();
@@ -350,10 +359,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DkdvSha
   if (wk0 < a.nk) mg.query_range(wk0, wk1, &wlo, &whi);
   const float sl2 = a.scale * kLog2e;
   const int t0 = range_tile_row(lo, BQ, 0);
+  DmaLanes<BQ, D, NT> dl(tid);
 
   auto load = [&](uint16_t* q_l, uint16_t* g_l, float* s_l, int r0) {
-    dma_tile<BQ, D, NT, SR>(q_l, Q, a.rq, r0, a.nq, tid);
-    dma_tile<BQ, D, NT, SR>(g_l, dO, a.rdo, r0, a.nq, tid);
+    dma_tile_lanes<BQ, D, NT, SR>(q_l, Q, a.rq, r0, a.nq, tid, dl.off);
+    dma_tile_lanes<BQ, D, NT, SR>(g_l, dO, a.rdo, r0, a.nq, tid, dl.off);
     if (wave < NH) dma_rows_f32x2(s_l + 64 * wave, LSE, DS, r0 + 32 * wave, a.nq, lane);
   };
   if (lo < hi) load(sQ0, sG0, sS0, t0);
@@ -909,6 +919,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   int lo, hi;
   mg.key_range(i0, i1, &lo, &hi);
   const int t0 = range_tile_row(lo, BN, 0);
+  DmaLanes<BN, D, NT> dl(tid);
 
   // running block cursor: index of key block `kbn`'s first dS block
   int kbn = t0 / 32;
@@ -950,19 +961,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   if (lo < hi) {
     V8 opA[NKB][2], opB[NKB][2];
     unsigned vA = 0, vB = 0;
-    dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
+    dma_tile_lanes<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid, dl.off);
     fetch(opA, vA);
     __syncthreads();
     for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
       if (j0 + BN < hi) {
-        dma_tile<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid);
+        dma_tile_lanes<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid, dl.off);
         fetch(opB, vB);
       }
       tile(sK0, opA, vA);
       __syncthreads();
       if (j0 + BN >= hi) break;
       if (j0 + 2 * BN < hi) {
-        dma_tile<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid);
+        dma_tile_lanes<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid, dl.off);
         fetch(opA, vA);
       }
       tile(sK1, opB, vB);
@@ -1014,10 +1025,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int rhi = qvalid ? mg.row_hi(myq) : 0;
   const float sl2 = a.scale * kLog2e;
   const int t0 = range_tile_row(lo, BN, 0);
+  DmaLanes<BN, D, NT> dl(tid);
 
   if (lo < hi) {
-    dma_tile<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid);
-    dma_tile<BN, D, NT, SR>(sV0, V, a.rv, t0, a.nk, tid);
+    dma_tile_lanes<BN, D, NT, SR>(sK0, K, a.rk, t0, a.nk, tid, dl.off);
+    dma_tile_lanes<BN, D, NT, SR>(sV0, V, a.rv, t0, a.nk, tid, dl.off);
   }
   V8 qop[KC], dop[KC];
   load_operand_rows<D, E>(qop, Q + rrow<SR, D>(a.rq, myq), qvalid, gq);
@@ -1068,15 +1080,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __syncthreads();
     for (int j0 = t0; j0 < hi; j0 += 2 * BN) {
       if (j0 + BN < hi) {
-        dma_tile<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid);
-        dma_tile<BN, D, NT, SR>(sV1, V, a.rv, j0 + BN, a.nk, tid);
+        dma_tile_lanes<BN, D, NT, SR>(sK1, K, a.rk, j0 + BN, a.nk, tid, dl.off);
+        dma_tile_lanes<BN, D, NT, SR>(sV1, V, a.rv, j0 + BN, a.nk, tid, dl.off);
       }
       tile(sK0, sV0, j0);
       __syncthreads();
       if (j0 + BN >= hi) break;
       if (j0 + 2 * BN < hi) {
-        dma_tile<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid);
-        dma_tile<BN, D, NT, SR>(sV0, V, a.rv, j0 + 2 * BN, a.nk, tid);
+        dma_tile_lanes<BN, D, NT, SR>(sK0, K, a.rk, j0 + 2 * BN, a.nk, tid, dl.off);
+        dma_tile_lanes<BN, D, NT, SR>(sV0, V, a.rv, j0 + 2 * BN, a.nk, tid, dl.off);
       }
       tile(sK1, sV1, j0 + BN);
       __syncthreads();

@@ -115,41 +115,125 @@ __device__ __forceinline__ typename E::v8 lds_tr8_at(const uint16_t* tile, int l
   return __builtin_bit_cast(typename E::v8, w);
 }
 
+// A pointer that every lane of the wave holds, marked wave-uniform so that
+// it lives in scalar registers.  Only for values that are the same in every
+// lane.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0; word 3 is
+// the gfx9 family's raw-buffer format field, 32-bit data).  Offsets at or
+// past `bytes` read as zero instead of reaching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // Direct global -> LDS load of a ROWS x D bf16 tile (rows r0 .. r0+ROWS-1 of
 // the n rows of a slice, addressed through `rm` from the slice base `src`)
-// into the tile layout, by NT threads.  gfx950's
-// global_load_lds_dwordx4 puts the 16 bytes each lane loads at the wave's LDS
-// base + 16 * lane, with no register staging: lane slot p is LDS chunk
-// position p, so the lane fetches the logical chunk that the layout stores
-// there; lanes on padding slots are switched off.  Rows >= n are filled from
-// row n - 1 (finite values that every kernel masks out); the first row r0
-// must be below n (contiguous rows address from row r0).  The loads count on
-// vmcnt; the caller waits for them (__syncthreads() does) before reading.
+// into the tile layout, by NT threads.  gfx950's buffer_load_dwordx4 ... lds
+// puts the 16 bytes each lane loads at the wave's LDS base (M0) + 16 * lane,
+// with no register staging: lane slot p is LDS chunk position p, so the lane
+// fetches the logical chunk that the layout stores there; lanes on padding
+// slots are switched off.  Rows >= n are filled from row n - 1 (finite
+// values that every kernel masks out); the first row r0 must be below n
+// (contiguous rows address from row r0).  The loads count on vmcnt; the
+// caller waits for them (__syncthreads() does) before reading.  `src`, r0
+// and n must be the same in every lane (they are read from the first active
+// lane).
+//
+// Addressing: a descriptor on a scalar base (contiguous rows: the tile's
+// first row), a 32-bit per-lane offset and a scalar LDS destination, so a
+// load costs no vector instruction beyond its offset -- which for every
+// tile but a slice's last (the only one with rows past the end, the only
+// one clamped) is a loop-invariant register.  The global-address form of
+// the load spent a 64-bit vector add per load, the compiler keeping each
+// offset as a 64-bit pair.
 template <int ROWS, int D, int NT, bool SR>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, const RowMap& rm,
                                          int r0, int n, int tid) {
   constexpr int CPR = D / 8, SPR = tstride<D>() / 8, TOTAL = ROWS * SPR;
   static_assert(TOTAL % 64 == 0, "whole waves per tile");
   constexpr int STEPS = (TOTAL + NT - 1) / NT;
-  // uniform base plus a 32-bit per-lane offset (the scalar-base addressing
-  // form of the load: one address VGPR per load instead of two)
-  // contiguous rows: the tile's first row goes into the scalar base
-  const uint16_t* base = SR ? src : src + (int64_t)r0 * D;
+  const char* base = uniform_ptr(SR ? src : src + (int64_t)r0 * D);
+  // the descriptor's range: the slice from `base` (32-bit byte offsets)
+  const int64_t span = SR ? (int64_t)0xffffffff : (int64_t)(n - r0) * (2 * D);
+  const __amdgpu_buffer_rsrc_t rsrc = raw_buffer(base, (uint32_t)min(span, (int64_t)0xffffffff));
   const int last = SR ? n - 1 : n - 1 - r0;
+  const int w0 = __builtin_amdgcn_readfirstlane(tid & ~63);  // the wave's first slot
+  auto issue = [&](auto clamp) {
 #pragma unroll
-  for (int t = 0; t < STEPS; ++t) {
-    const int wbase = t * NT + (tid & ~63);  // first slot of this wave's 64
-    if (wbase < TOTAL) {
-      const int p = wbase + (tid & 63);
-      const int row = p / SPR, phys = p % SPR;
-      if (phys < CPR) {
-        const int ch = phys ^ ((row >> 2) & 3);
-        const uint32_t off = SR ? 2u * rm.row(min(r0 + row, last)) + (uint32_t)(ch * 16)
-                                : (uint32_t)(min(row, last) * (2 * D) + ch * 16);  // bytes
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)((const char*)base + off),
-            (__attribute__((address_space(3))) void*)(lds + wbase * 8), 16, 0, 0);
+    for (int t = 0; t < STEPS; ++t) {
+      const int wbase = t * NT + w0;
+      if (wbase < TOTAL) {
+        const int p = t * NT + tid;  // slot wbase + lane
+        const int row = p / SPR, phys = p % SPR;
+        if (phys < CPR) {
+          const int ch = phys ^ ((row >> 2) & 3);
+          int rr = SR ? r0 + row : row;
+          if constexpr (decltype(clamp)::value) rr = min(rr, last);
+          const uint32_t off = SR ? 2u * rm.row(rr) + (uint32_t)(ch * 16)
+                                  : (uint32_t)(rr * (2 * D) + ch * 16);  // bytes
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rsrc, (__attribute__((address_space(3))) void*)(lds + wbase * 8), 16, off, 0, 0, 0);
+        }
       }
+    }
+  };
+  if (r0 + ROWS <= n)
+    issue(std::false_type{});
+  else
+    issue(std::true_type{});
+}
+
+// dma_tile's per-lane addressing for tiles of contiguous rows, computed once
+// per kernel and kept in registers: for each load step of a ROWS x D tile,
+// the byte offset of the lane's chunk from the tile's first row, or kDmaPad
+// on padding slots (past every tile, so the descriptor's range check drops
+// those loads and no exec-mask branch is needed).
+constexpr uint32_t kDmaPad = 0x40000000u;
+template <int ROWS, int D, int NT>
+struct DmaLanes {
+  static constexpr int CPR = D / 8, SPR = tstride<D>() / 8, TOTAL = ROWS * SPR;
+  static constexpr int STEPS = (TOTAL + NT - 1) / NT;
+  uint32_t off[STEPS];
+  __device__ __forceinline__ explicit DmaLanes(int tid) {
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      const int p = t * NT + tid, row = p / SPR, phys = p % SPR;
+      off[t] = (p < TOTAL && phys < CPR) ? (uint32_t)(row * (2 * D) + (phys ^ ((row >> 2) & 3)) * 16)
+                                         : kDmaPad;
+    }
+  }
+};
+
+// dma_tile with lane offsets precomputed by DmaLanes<ROWS, D, NT> (`off`
+// is its array): a tile whose rows all lie below n (every tile of a slice but
+// possibly its last) takes one load per step and no vector instruction; the
+// rest go through the general path.  The offsets pass through an empty asm
+// at each use so that the compiler keeps them in registers rather than
+// recomputing them at every load.
+template <int ROWS, int D, int NT, bool SR>
+__device__ __forceinline__ void dma_tile_lanes(uint16_t* lds, const uint16_t* src, const RowMap& rm,
+                                               int r0, int n, int tid, uint32_t* off) {
+  using DL = DmaLanes<ROWS, D, NT>;
+  if (SR || r0 + ROWS > n) {
+    dma_tile<ROWS, D, NT, SR>(lds, src, rm, r0, n, tid);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rsrc =
+      raw_buffer(uniform_ptr(src + (int64_t)r0 * D), (uint32_t)(ROWS * 2 * D));
+  const int w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+#pragma unroll
+  for (int t = 0; t < DL::STEPS; ++t) {
+    const int wbase = t * NT + w0;
+    if (DL::TOTAL % NT == 0 || wbase < DL::TOTAL) {
+      asm volatile("" : "+v"(off[t]));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(lds + wbase * 8), 16, off[t], 0, 0, 0);
     }
   }
 }
