@@ -164,7 +164,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
         s[mb][e] = p;
         rs += p;
       }
-    rs = sum_halves(rs);
     l += rs;
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c) {
@@ -218,7 +217,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
       sc[e] = p;
       rs += p;
     }
-    rs = sum_halves(rs);
     l += rs;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
@@ -265,6 +263,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
   // every wave is past its last LDS read here (each path above ends in a
   // barrier, and with no visible key no tile was loaded): O rows go through
   // sK0 (waves 0, 1) and sV0 (waves 2, 3) for whole-row 16-byte stores
+  // each lane's l holds the sums of its half of the row's keys (the two
+  // halves share m, so every rescale applied to both): combined once here
+  l = sum_halves(l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   acc_to_lds<D, E>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), oacc, inv, gq);
   if (qvalid && gq == 0)

@@ -206,6 +206,9 @@ struct DmaLanes {
       const int p = t * NT + tid, row = p / SPR, phys = p % SPR;
       off[t] = (p < TOTAL && phys < CPR) ? (uint32_t)(row * (2 * D) + (phys ^ ((row >> 2) & 3)) * 16)
                                          : kDmaPad;
+      // opaque from here on: the compiler keeps the value in a register
+      // instead of recomputing it at each load
+      asm volatile("" : "+v"(off[t]));
     }
   }
 };
@@ -213,9 +216,7 @@ struct DmaLanes {
 // dma_tile with lane offsets precomputed by DmaLanes<ROWS, D, NT> (`off`
 // is its array): a tile whose rows all lie below n (every tile of a slice but
 // possibly its last) takes one load per step and no vector instruction; the
-// rest go through the general path.  The offsets pass through an empty asm
-// at each use so that the compiler keeps them in registers rather than
-// recomputing them at every load.
+// rest go through the general path.
 template <int ROWS, int D, int NT, bool SR>
 __device__ __forceinline__ void dma_tile_lanes(uint16_t* lds, const uint16_t* src, const RowMap& rm,
                                                int r0, int n, int tid, uint32_t* off) {
@@ -231,7 +232,6 @@ __device__ __forceinline__ void dma_tile_lanes(uint16_t* lds, const uint16_t* sr
   for (int t = 0; t < DL::STEPS; ++t) {
     const int wbase = t * NT + w0;
     if (DL::TOTAL % NT == 0 || wbase < DL::TOTAL) {
-      asm volatile("" : "+v"(off[t]));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsrc, (__attribute__((address_space(3))) void*)(lds + wbase * 8), 16, off[t], 0, 0, 0);
     }
