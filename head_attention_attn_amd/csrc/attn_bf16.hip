@@ -260,12 +260,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((SB && 
       __syncthreads();
     }
   }
-  // every wave is past its last LDS read here (each path above ends in a
-  // barrier, and with no visible key no tile was loaded): O rows go through
-  // sK0 (waves 0, 1) and sV0 (waves 2, 3) for whole-row 16-byte stores
   // each lane's l holds the sums of its half of the row's keys (the two
   // halves share m, so every rescale applied to both): combined once here
   l = sum_halves(l);
+  // every wave is past its last LDS read here (each path above ends in a
+  // barrier, and with no visible key no tile was loaded): O rows go through
+  // sK0 (waves 0, 1) and sV0 (waves 2, 3) for whole-row 16-byte stores
   const float inv = l > 0.f ? 1.f / l : 0.f;
   acc_to_lds<D, E>(wave < 2 ? sK0 : sV0, 32 * (wave & 1) + (lane & 31), oacc, inv, gq);
   if (qvalid && gq == 0)

@@ -147,11 +147,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const char* base, u
 //
 // Addressing: a descriptor on a scalar base (contiguous rows: the tile's
 // first row), a 32-bit per-lane offset and a scalar LDS destination, so a
-// load costs no vector instruction beyond its offset -- which for every
-// tile but a slice's last (the only one with rows past the end, the only
-// one clamped) is a loop-invariant register.  The global-address form of
-// the load spent a 64-bit vector add per load, the compiler keeping each
-// offset as a 64-bit pair.
+// load costs no vector instruction beyond its offset, which this general
+// form computes per load (clamped only in a tile with rows past the slice's
+// end); dma_tile_lanes holds the offsets in registers instead.  The
+// global-address form of the load spent a 64-bit vector add per load, the
+// compiler keeping each offset as a 64-bit pair.
 template <int ROWS, int D, int NT, bool SR>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* src, const RowMap& rm,
                                          int r0, int n, int tid) {
