@@ -87,16 +87,17 @@ def test_bf16_lengths(n, mask, window, d):
     parity_case(1, 3, n, n, d, "bf16", mask, window, seed=n)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 96])
 @pytest.mark.parametrize("n", [333, 513])
 @pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 100)])
-def test_bf16_long_general_passes(d, n, mask, window):
+def test_long_general_passes(d, n, mask, window, dtype):
     """d = 64, 96 past the short-sequence bounds: more than 256 keys take the
     forward's double-buffered tile loop, more than 224 the general dK/dV pass
     and the recomputing dQ pass.  Several 64-row tiles whose loads take the
     in-range path and a ragged last tile that takes the clamped one, against
-    the oracle."""
-    parity_case(1, 2, n, n, d, "bf16", mask, window, seed=n + d)
+    the oracle within the input type's tolerance."""
+    parity_case(1, 2, n, n, d, dtype, mask, window, seed=n + d)
 
 
 @pytest.mark.parametrize("nq,nk,mask,window", [
